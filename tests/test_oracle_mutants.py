@@ -1,0 +1,54 @@
+"""Plant plausible mistakes in copies of the oracle and check that the pins catch each.
+
+Every mutant is a one-place textual change to ``oracle/attn_oracle.c`` (a dropped term,
+a wrong sign, index or bound, a transposed or swapped operand), compiled on the CPU
+into a temporary library.  The real oracle is never modified.  A mutant that no pin
+rejects would mean the pins leave that part of the oracle unchecked.
+"""
+import pytest
+
+import oracle
+from pins import PINS
+
+MUTANTS = {
+    "drop_scale": ("scores[j] = P->scale * dot;", "scores[j] = dot;"),
+    "causal_excludes_diagonal": ("if (causal && j > p) return 0;", "if (causal && j >= p) return 0;"),
+    "bidir_band_too_narrow": ("if (d > half) return 0;", "if (d >= half) return 0;"),
+    "causal_band_too_wide": ("if (p - j >= P->window) return 0;", "if (p - j > P->window) return 0;"),
+    "kv_head_interleaved": ("const int kh = h / group;", "const int kh = h % P->kv_heads;"),
+    "k_transposed": ("load_elem(P->k, P->dtype, k_row + d)",
+                     "load_elem(P->k, P->dtype, kv_head_base * D + (int64_t)d * P->kv_stride + j)"),
+    "no_normalisation": ("const double pj = scores[j] / z;", "const double pj = scores[j];"),
+    "exp_sign_flipped": ("scores[j] = exp(scores[j] - m);", "scores[j] = exp(m - scores[j]);"),
+    "padding_not_masked": ("*nvalid = len;\n    *pos = (int64_t)P->pos_offset + i;",
+                           "*nvalid = P->kv_len;\n    *pos = (int64_t)P->pos_offset + i;"),
+    "pos_offset_dropped": ("*pos = (int64_t)P->pos_offset + i;", "*pos = (int64_t)i;"),
+    "padded_rows_attend": ("if (p >= nvalid) return 0; /* padded query row */", ""),
+    "decode_query_one_late": ("*pos = len - 1;", "*pos = len;"),
+    "decode_not_causal": ("int causal = P->decode ? 1 : P->causal;", "int causal = P->decode ? 0 : P->causal;"),
+    "v_read_from_k": ("load_elem(P->v, P->dtype, v_row + d)", "load_elem(P->k, P->dtype, v_row + d)"),
+    "q_head_uses_kv_index": ("(((int64_t)b * P->q_heads + h) * P->q_len + i) * D",
+                             "(((int64_t)b * P->q_heads + kh) * P->q_len + i) * D"),
+    "last_dim_dropped": ("for (int d = 0; d < D; ++d)\n            dot +=",
+                         "for (int d = 0; d < D - 1; ++d)\n            dot +="),
+    "bf16_low_half": ("uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;",
+                      "uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 15;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = oracle.SOURCE.read_text()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(src.replace(old, new))
+    lib = oracle.compile_library(mutant_src, tmp_path / "libmutant.so")
+    m = oracle.Oracle(lib)
+    caught = []
+    for pin_name, pin in PINS.items():
+        try:
+            pin(m)
+        except (AssertionError, ValueError):
+            caught.append(pin_name)
+    assert caught, f"no pin rejects the mutant {name}"
