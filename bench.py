@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass over the whole path on resident synthetic inputs:
+  * prefill: causal GQA attention, batch 1, 32 query / 8 KV heads, head_dim 128,
+    q_len = kv_len = 4096, bf16 (the MFMA-bound kernel);
+  * decode: one token per (item, query head), batch 64, 32/8 heads, head_dim 128, over
+    a head-major bf16 KV cache of 8192 positions (the HBM-bound kernels).
+Prints one JSON line.  `value` is the prefill throughput in TFLOP/s of algorithmic work
+(4 * head_dim per unmasked query-key pair); the decode KV-cache bandwidth rides on the
+same line, each with a roofline object.  Kernel times come from HIP events recorded on
+the stream the kernels run on.  `--workload` benchmarks one other named workload alone.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+import workloads as W  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (vector)
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PROFILES = ROOT / "profiles"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work
+
+
+def keys_per_row(w: W.Workload, seq_lens) -> np.ndarray:
+    """Number of keys in the key set of every query row: [batch, q_len]."""
+    pos = w.pos_offset + np.arange(w.q_len)
+    counts = np.zeros((w.batch, w.q_len), np.int64)
+    for b in range(w.batch):
+        valid = w.kv_len if seq_lens is None else min(max(int(seq_lens[b]), 0), w.kv_len)
+        if w.causal:
+            hi = np.minimum(pos, valid - 1)
+            lo = np.zeros_like(pos) if w.window == 0 else np.maximum(0, pos - w.window + 1)
+        else:
+            hi = np.full_like(pos, valid - 1) if w.window == 0 else np.minimum(valid - 1, pos + w.window // 2)
+            lo = np.zeros_like(pos) if w.window == 0 else np.maximum(0, pos - w.window // 2)
+        c = np.maximum(0, hi - lo + 1)
+        c[pos >= valid] = 0
+        counts[b] = c
+    return counts
+
+
+def prefill_flops(w: W.Workload, seq_lens) -> float:
+    return 4.0 * w.head_dim * w.q_heads * float(keys_per_row(w, seq_lens).sum())
+
+
+def prefill_bytes(w: W.Workload, seq_lens) -> float:
+    """Q + valid K/V rows + O, each once."""
+    esz = 2 if w.dtype == "bf16" else 4
+    valid = np.full(w.batch, w.kv_len) if seq_lens is None else np.clip(seq_lens, 0, w.kv_len)
+    kv = 2.0 * w.kv_heads * w.head_dim * esz * float(valid.sum())
+    qo = 2.0 * w.batch * w.q_heads * w.q_len * w.head_dim * esz
+    return kv + qo
+
+
+def decode_bytes(w: W.Workload) -> float:
+    esz = 2 if w.dtype == "bf16" else 4
+    keys = min(w.pos_offset + 1, w.kv_len)
+    kv = 2.0 * w.batch * w.kv_heads * keys * w.head_dim * esz
+    qo = 2.0 * w.batch * w.q_heads * w.head_dim * esz
+    return kv + qo
+
+
+def decode_flops(w: W.Workload) -> float:
+    return 4.0 * w.head_dim * w.batch * w.q_heads * min(w.pos_offset + 1, w.kv_len)
+
+
+# ---------------------------------------------------------------------------
+# device side
+
+
+def to_gpu(a: np.ndarray):
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
+    return torch.from_numpy(a).to("cuda")
+
+
+class Runner:
+    """Holds one workload's resident device inputs and launches it."""
+
+    def __init__(self, w: W.Workload, x: dict):
+        import torch
+        import head_attention_02_amd as mi
+        self.mi, self.w = mi, w
+        self.q, self.k, self.v = to_gpu(x["q"]), to_gpu(x["k"]), to_gpu(x["v"])
+        self.out = torch.empty_like(self.q)
+        lens = x.get("seq_lens") if w.kind == "prefill" else x.get("kv_lens")
+        self.lens = None if lens is None else to_gpu(lens)
+        self.ws = None
+        if w.kind == "decode":
+            n = mi.attn_decode_workspace_bytes(w.batch, w.q_heads, w.kv_heads, w.kv_len, w.head_dim)
+            self.ws = torch.empty(max(n, 16), dtype=torch.uint8, device="cuda")
+
+    def __call__(self):
+        w = self.w
+        if w.kind == "prefill":
+            self.mi.attn_prefill(self.q, self.k, self.v, self.out, pos_offset=w.pos_offset, seq_lens=self.lens,
+                                 window=w.window, causal=w.causal, scale=w.attn_scale)
+        else:
+            self.mi.attn_decode(self.q, self.k, self.v, self.out, kv_len=w.kv_len, pos_offset=w.pos_offset,
+                                kv_lens=self.lens, window=w.window, scale=w.attn_scale, workspace=self.ws)
+
+
+def kernel_sources_digest(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        h.update((ROOT / "head_attention_02_amd" / "csrc" / n).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(key: str, digest: str):
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/traffic.json), or
+    None when the kernel source changed since the counters were taken."""
+    f = PROFILES / "traffic.json"
+    if not f.exists():
+        return None
+    rec = json.loads(f.read_text()).get(key)
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, timed on the host cores on a bounded sample
+
+
+def cpu_baseline_prefill(w: W.Workload, x: dict, budget_s: float) -> dict:
+    import oracle
+    ref = oracle.default()
+    nt = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(123)
+    total = w.batch * w.q_heads * w.q_len
+    perm = rng.permutation(total)
+    rows_all = np.stack([perm // (w.q_heads * w.q_len), (perm // w.q_len) % w.q_heads, perm % w.q_len], 1)
+    counts = keys_per_row(w, x["seq_lens"])
+    kw = dict(scale=w.attn_scale, causal=w.causal, pos_offset=w.pos_offset, seq_lens=x["seq_lens"], window=w.window)
+    n = min(64, total)
+    while True:
+        rows = rows_all[:n].astype(np.int32)
+        t0 = time.perf_counter()
+        ref.prefill(x["q"], x["k"], x["v"], rows=rows, nthreads=nt, **kw)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 4 or n == total:
+            break
+        n = min(total, max(n * 2, int(n * budget_s / max(dt, 1e-3))))
+    flops = 4.0 * w.head_dim * float(counts[rows[:, 0], rows[:, 2]].sum())
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": ref.threads_used, "kind": "oracle",
+            "sample": f"{n} of {total} query rows of {w.name} (uniform random), fp64, {dt:.1f} s"}
+
+
+def cpu_baseline_decode(w: W.Workload, x: dict, budget_s: float) -> dict:
+    import oracle
+    ref = oracle.default()
+    nt = len(os.sched_getaffinity(0))
+    total = w.batch * w.q_heads
+    rng = np.random.default_rng(321)
+    perm = rng.permutation(total)
+    pairs_all = np.stack([perm // w.q_heads, perm % w.q_heads], 1)
+    n = min(8, total)
+    while True:
+        pairs = pairs_all[:n].astype(np.int32)
+        t0 = time.perf_counter()
+        ref.decode(x["q"], x["k"], x["v"], kv_len=w.kv_len, scale=w.attn_scale, pos_offset=w.pos_offset,
+                   window=w.window, rows=pairs, nthreads=nt)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 4 or n == total:
+            break
+        n = min(total, max(n * 2, int(n * budget_s / max(dt, 1e-3))))
+    esz = 2 if w.dtype == "bf16" else 4
+    # bytes of K and V each query row streams (the GPU reads each once per KV head group)
+    by = 2.0 * n * min(w.pos_offset + 1, w.kv_len) * w.head_dim * esz
+    return {"value": by / dt / 1e9, "unit": "GB/s", "cores": ref.threads_used, "kind": "oracle",
+            "sample": f"{n} of {total} (item, query head) rows of {w.name}, fp64, {dt:.1f} s"}
+
+
+# ---------------------------------------------------------------------------
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="headline",
+                    help="headline (prefill causal_gqa_s4096 + decode gqa_decode_kv8192) or a name in workloads.WORKLOADS")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work per baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this attention library runs on one GPU; --gpus must be 1"}))
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+    import head_attention_02_amd as mi
+    mi.library()
+
+    if args.workload == "headline":
+        names = ["causal_gqa_s4096", "gqa_decode_kv8192"]
+    else:
+        names = [args.workload]
+    ws = [W.WORKLOADS[n] for n in names]
+    inputs, runners = [], []
+    for w in ws:
+        log(f"generating {w.name}")
+        x = W.make_inputs(w)
+        inputs.append(x)
+        runners.append(Runner(w, x))
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        for r in runners:
+            r()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(runners) + 1)] for _ in range(K)]
+    begin, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(1_000_000)   # keep the queue ahead of the GPU so events time kernels, not launches
+    t0 = time.perf_counter()
+    begin.record()
+    for s in range(K):
+        ev[s][0].record()
+        for i, r in enumerate(runners):
+            r()
+            ev[s][i + 1].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = begin.elapsed_time(end) / K
+    kernel_ms = [float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)])) for i in range(len(runners))]
+
+    result = {"metric": "attention TFLOP/s (prefill, % MFMA peak); decode KV GB/s (% HBM peak)",
+              "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": step_ms,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+              "data": "synthetic (seeded N(0, sigma^2), bf16 by round-to-nearest-even)"}
+    rooflines = {}
+    for w, x, ms in zip(ws, inputs, kernel_ms):
+        sec = ms / 1e3
+        if w.kind == "prefill":
+            fl = prefill_flops(w, x["seq_lens"])
+            peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+            src = ["prefill_bf16.hip" if w.dtype == "bf16" else "prefill_f32.hip", "mi_attn_device.hpp"]
+            rooflines[w.name] = {"bound": "mfma", "achieved": fl / sec / 1e12, "peak": peak, "unit": "TFLOP/s",
+                                 "frac": fl / sec / 1e12 / peak,
+                                 "traffic": traffic_from_profiles(w.name, kernel_sources_digest(src)),
+                                 "kernel_ms": ms, "algorithmic_flop": fl,
+                                 "algorithmic_bytes": prefill_bytes(w, x["seq_lens"]),
+                                 "hbm_GBps": prefill_bytes(w, x["seq_lens"]) / sec / 1e9}
+        else:
+            by = decode_bytes(w)
+            src = ["decode.hip", "mi_attn_device.hpp"]
+            rooflines[w.name] = {"bound": "hbm", "achieved": by / sec / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                 "frac": by / sec / 1e9 / PEAK_HBM_GBPS,
+                                 "traffic": traffic_from_profiles(w.name, kernel_sources_digest(src)),
+                                 "kernel_ms": ms, "algorithmic_bytes": by,
+                                 "algorithmic_flop": decode_flops(w)}
+    head = ws[0]
+    r0 = rooflines[head.name]
+    result["value"] = r0["achieved"]
+    result["unit"] = r0["unit"]
+    result["dtype"] = head.dtype
+    result["roofline"] = {k: r0[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+    if len(ws) > 1:
+        r1 = rooflines[ws[1].name]
+        result["decode_kv_GBps"] = r1["achieved"]
+        result["roofline_decode"] = {k: r1[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+    result["config"] = {"workload": " + ".join(f"{w.kind} {w.name}" for w in ws),
+                        "detail": {w.name: {"batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+                                            "q_len": w.q_len, "kv_len": w.kv_len, "head_dim": w.head_dim,
+                                            "causal": w.causal, "window": w.window, "pos_offset": w.pos_offset,
+                                            "dtype": w.dtype} for w in ws},
+                        "kernels": rooflines}
+    result["wall_s_timed_region"] = wall
+
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (cpu_baseline)")
+        for w, x in zip(ws, inputs):
+            if w.kind == "prefill":
+                result.setdefault("cpu_baseline", cpu_baseline_prefill(w, x, args.cpu_budget))
+            else:
+                key = "cpu_baseline" if "cpu_baseline" not in result else "cpu_baseline_decode"
+                result[key] = cpu_baseline_decode(w, x, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,177 @@
+"""Python binding of libmi_attn (MI355X / gfx950 attention).
+
+Argument marshalling only: each function checks the tensors it is given, turns them
+into device pointers and sizes, and calls the C entry point of the same name
+(declared in include/mi_attn.h) on the current HIP stream.  Every step of the
+computation runs in the library's kernels; there is no fallback of any kind, and a
+missing library or GPU raises.
+
+    attn_prefill(q, k, v, out=None, *, pos_offset=0, seq_lens=None, window=0,
+                 causal=False, scale=None)
+    attn_decode(q, k_cache, v_cache, out=None, *, kv_len=None, pos_offset=None,
+                kv_lens=None, window=0, scale=None, workspace=None)
+    attn_decode_workspace_bytes(batch, q_heads, kv_heads, kv_len, head_dim)
+    attn_last_error(), attn_version()
+
+Layouts: q [batch, q_heads, q_len, head_dim]; k, v [batch, kv_heads, kv_len, head_dim];
+decode caches [batch, kv_heads, capacity, head_dim] (head-major).  scale defaults to
+1/sqrt(head_dim).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from pathlib import Path
+
+LIBRARY = Path(__file__).resolve().parent / "libmi_attn.so"
+
+MI_ATTN_F32, MI_ATTN_BF16 = 0, 1
+MI_ATTN_OK, MI_ATTN_ERR_INVALID, MI_ATTN_ERR_UNSUPPORTED, MI_ATTN_ERR_HIP = 0, 1, 2, 3
+
+EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_workspace_bytes", "attn_last_error", "attn_version")
+
+
+class MiAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[status {status}] {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libmi_attn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not LIBRARY.exists():
+            raise RuntimeError(f"{LIBRARY} is not built; run `python -m head_attention_02_amd.build`")
+        lib = ctypes.CDLL(str(LIBRARY))
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.attn_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, i, i, f, i, vp]
+        lib.attn_prefill.restype = i
+        lib.attn_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, i, f, i, vp, sz, vp]
+        lib.attn_decode.restype = i
+        lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+        lib.attn_decode_workspace_bytes.restype = sz
+        lib.attn_last_error.argtypes = []
+        lib.attn_last_error.restype = ctypes.c_char_p
+        lib.attn_version.argtypes = []
+        lib.attn_version.restype = i
+        _lib = lib
+    return _lib
+
+
+def attn_version() -> int:
+    return library().attn_version()
+
+
+def attn_last_error() -> str:
+    return library().attn_last_error().decode()
+
+
+def attn_decode_workspace_bytes(batch: int, q_heads: int, kv_heads: int, kv_len: int, head_dim: int) -> int:
+    return int(library().attn_decode_workspace_bytes(batch, q_heads, kv_heads, kv_len, head_dim))
+
+
+def _check(status: int) -> None:
+    if status != MI_ATTN_OK:
+        raise MiAttnError(status, attn_last_error())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return MI_ATTN_BF16
+    if t.dtype == torch.float32:
+        return MI_ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev(t, name: str, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def attn_prefill(q, k, v, out=None, *, pos_offset: int = 0, seq_lens=None, window: int = 0,
+                 causal: bool = False, scale: float | None = None, stream=None):
+    """Prefill attention; returns `out` [batch, q_heads, q_len, head_dim]."""
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B,Hq,Lq,D] and k, v [B,Hkv,Lk,D]")
+    B, Hq, Lq, D = q.shape
+    Bk, Hkv, Lk, Dk = k.shape
+    if Bk != B or Dk != D:
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree on batch or head_dim")
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    if seq_lens is not None and (seq_lens.dtype != torch.int32 or seq_lens.numel() != B):
+        raise ValueError("seq_lens must be an int32 tensor of batch elements")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = library().attn_prefill(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), B, Hq, Hkv, Lq, Lk,
+                                D, pos_offset, _dev(seq_lens, "seq_lens"), window, int(bool(causal)),
+                                float(scale), dt, _stream(stream))
+    _check(st)
+    return out
+
+
+def attn_decode(q, k_cache, v_cache, out=None, *, kv_len: int | None = None, pos_offset: int | None = None,
+                kv_lens=None, window: int = 0, scale: float | None = None, workspace=None, stream=None):
+    """Decode attention of one token per (item, head); returns `out` [batch, q_heads, head_dim]."""
+    torch = _torch()
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B,Hq,D] and the caches [B,Hkv,capacity,D]")
+    B, Hq, D = q.shape
+    Bk, Hkv, cap, Dk = k_cache.shape
+    if Bk != B or Dk != D:
+        raise ValueError("q and the caches disagree on batch or head_dim")
+    dt = _dtype_code(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    if kv_len is None:
+        kv_len = cap
+    if pos_offset is None:
+        pos_offset = kv_len - 1
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    if kv_lens is not None and (kv_lens.dtype != torch.int32 or kv_lens.numel() != B):
+        raise ValueError("kv_lens must be an int32 tensor of batch elements")
+    need = attn_decode_workspace_bytes(B, Hq, Hkv, kv_len, D) if Hq % Hkv == 0 else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = library().attn_decode(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(out, "out"),
+                               B, Hq, Hkv, kv_len, cap, D, pos_offset, _dev(kv_lens, "kv_lens"), window,
+                               float(scale), dt, _dev(workspace, "workspace"), ws_bytes, _stream(stream))
+    _check(st)
+    return out

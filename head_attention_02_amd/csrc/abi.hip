@@ -1,0 +1,162 @@
+// abi.hip -- the extern "C" entry points of libmi_attn: argument validation, launch
+// planning and dispatch to the gfx950 kernels.  Declarations and their documentation
+// are in include/mi_attn.h.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <cmath>
+
+#include "mi_attn.h"
+#include "mi_attn_kernels.hpp"
+
+namespace {
+
+thread_local char g_error[512];
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_error, sizeof g_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool supported_head_dim(int d) { return d == 32 || d == 64 || d == 128; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_version(void) { return MI_ATTN_VERSION; }
+
+const char* attn_last_error(void) { return g_error; }
+
+int attn_prefill(const void* q, const void* k, const void* v, void* out, int batch, int q_heads,
+                 int kv_heads, int q_len, int kv_len, int head_dim, int pos_offset,
+                 const int32_t* seq_lens, int window, int causal, float scale, int dtype,
+                 void* stream) {
+    g_error[0] = '\0';
+    const char* fn = "attn_prefill";
+    if (dtype != MI_ATTN_BF16 && dtype != MI_ATTN_F32)
+        return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+    if (batch < 0 || q_len < 0 || kv_len < 0)
+        return fail(MI_ATTN_ERR_INVALID, "%s: negative size (batch %d, q_len %d, kv_len %d)", fn, batch,
+                    q_len, kv_len);
+    if (q_heads < 1 || kv_heads < 1)
+        return fail(MI_ATTN_ERR_INVALID, "%s: q_heads (%d) and kv_heads (%d) must be >= 1", fn, q_heads,
+                    kv_heads);
+    if (q_heads % kv_heads != 0)
+        return fail(MI_ATTN_ERR_INVALID, "%s: q_heads (%d) is not a multiple of kv_heads (%d)", fn, q_heads,
+                    kv_heads);
+    if (pos_offset < 0 || (long)pos_offset + q_len > kv_len)
+        return fail(MI_ATTN_ERR_INVALID, "%s: pos_offset (%d) + q_len (%d) exceeds kv_len (%d)", fn,
+                    pos_offset, q_len, kv_len);
+    if (window < 0) return fail(MI_ATTN_ERR_INVALID, "%s: window (%d) is negative", fn, window);
+    if (!std::isfinite(scale)) return fail(MI_ATTN_ERR_INVALID, "%s: scale is not finite", fn);
+    if (!supported_head_dim(head_dim))
+        return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: head_dim %d is not one of 32, 64, 128", fn, head_dim);
+    if (batch == 0 || q_len == 0) return MI_ATTN_OK;
+    if (!q || !k || !v || !out) return fail(MI_ATTN_ERR_INVALID, "%s: null tensor pointer", fn);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(MI_ATTN_ERR_INVALID, "%s: tensors must be 16-byte aligned", fn);
+    if (seq_lens && ((uintptr_t)seq_lens & 3u))
+        return fail(MI_ATTN_ERR_INVALID, "%s: seq_lens must be 4-byte aligned", fn);
+    if ((long)q_heads > 65535 || (long)batch > 65535)
+        return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: q_heads and batch must be <= 65535", fn);
+
+    mi_attn::PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.seq_lens = seq_lens;
+    a.batch = batch;
+    a.q_heads = q_heads;
+    a.kv_heads = kv_heads;
+    a.q_len = q_len;
+    a.kv_len = kv_len;
+    a.pos_offset = pos_offset;
+    a.window = window;
+    a.causal = causal ? 1 : 0;
+    a.scale = scale;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = dtype == MI_ATTN_BF16 ? mi_attn::launch_prefill_bf16(a, head_dim, s)
+                                         : mi_attn::launch_prefill_f32(a, head_dim, s);
+    if (e != hipSuccess) return fail(MI_ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return MI_ATTN_OK;
+}
+
+size_t attn_decode_workspace_bytes(int batch, int q_heads, int kv_heads, int kv_len, int head_dim) {
+    if (batch <= 0 || q_heads < 1 || kv_heads < 1 || q_heads % kv_heads || kv_len < 1 ||
+        !supported_head_dim(head_dim))
+        return 0;
+    const mi_attn::DecodePlan p = mi_attn::plan_decode(batch, q_heads, kv_heads, kv_len, head_dim);
+    return (size_t)batch * q_heads * p.splits * (head_dim + 2) * sizeof(float);
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* out, int batch,
+                int q_heads, int kv_heads, int kv_len, int capacity, int head_dim, int pos_offset,
+                const int32_t* kv_lens, int window, float scale, int dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    g_error[0] = '\0';
+    const char* fn = "attn_decode";
+    if (dtype != MI_ATTN_BF16 && dtype != MI_ATTN_F32)
+        return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+    if (batch < 0) return fail(MI_ATTN_ERR_INVALID, "%s: negative batch (%d)", fn, batch);
+    if (q_heads < 1 || kv_heads < 1)
+        return fail(MI_ATTN_ERR_INVALID, "%s: q_heads (%d) and kv_heads (%d) must be >= 1", fn, q_heads,
+                    kv_heads);
+    if (q_heads % kv_heads != 0)
+        return fail(MI_ATTN_ERR_INVALID, "%s: q_heads (%d) is not a multiple of kv_heads (%d)", fn, q_heads,
+                    kv_heads);
+    if (kv_len < 1 || kv_len > capacity)
+        return fail(MI_ATTN_ERR_INVALID, "%s: need 1 <= kv_len (%d) <= capacity (%d)", fn, kv_len, capacity);
+    if (!kv_lens && (pos_offset < 0 || pos_offset >= kv_len))
+        return fail(MI_ATTN_ERR_INVALID, "%s: pos_offset (%d) must lie in [0, kv_len %d)", fn, pos_offset,
+                    kv_len);
+    if (window < 0) return fail(MI_ATTN_ERR_INVALID, "%s: window (%d) is negative", fn, window);
+    if (!std::isfinite(scale)) return fail(MI_ATTN_ERR_INVALID, "%s: scale is not finite", fn);
+    if (!supported_head_dim(head_dim))
+        return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: head_dim %d is not one of 32, 64, 128", fn, head_dim);
+    if (batch == 0) return MI_ATTN_OK;
+    if (!q || !k_cache || !v_cache || !out) return fail(MI_ATTN_ERR_INVALID, "%s: null tensor pointer", fn);
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return fail(MI_ATTN_ERR_INVALID, "%s: tensors must be 16-byte aligned", fn);
+    if (kv_lens && ((uintptr_t)kv_lens & 3u))
+        return fail(MI_ATTN_ERR_INVALID, "%s: kv_lens must be 4-byte aligned", fn);
+    if ((long)batch > 65535 || (long)q_heads > 65535)
+        return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: q_heads and batch must be <= 65535", fn);
+    const size_t need = attn_decode_workspace_bytes(batch, q_heads, kv_heads, kv_len, head_dim);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(MI_ATTN_ERR_INVALID, "%s: workspace of %zu bytes given, %zu needed", fn, workspace_bytes,
+                    need);
+    if (!aligned16(workspace)) return fail(MI_ATTN_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
+
+    const mi_attn::DecodePlan p = mi_attn::plan_decode(batch, q_heads, kv_heads, kv_len, head_dim);
+    mi_attn::DecodeArgs a{};
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.out = out;
+    a.ws = (float*)workspace;
+    a.kv_lens = kv_lens;
+    a.batch = batch;
+    a.q_heads = q_heads;
+    a.kv_heads = kv_heads;
+    a.kv_len = kv_len;
+    a.capacity = capacity;
+    a.pos_offset = pos_offset;
+    a.window = window;
+    a.scale = scale;
+    a.splits = p.splits;
+    a.split_len = p.split_len;
+    a.head_groups = p.head_groups;
+    hipError_t e = mi_attn::launch_decode(a, head_dim, p.heads_per_group, dtype == MI_ATTN_BF16,
+                                          (hipStream_t)stream);
+    if (e != hipSuccess) return fail(MI_ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return MI_ATTN_OK;
+}
+
+}  // extern "C"

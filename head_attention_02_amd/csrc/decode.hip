@@ -1,0 +1,259 @@
+// decode.hip -- single-token attention over a head-major KV cache (split-KV).
+//
+// The operation is `flash_attention_batched_per_cache` of the ferrum-kernels `Backend`
+// page: one query token per (item, query head) against that item's cache
+// [kv_heads, capacity, head_dim], with per-item lengths read on the device and an
+// optional causal window (the last w positions).  It is bound by HBM bandwidth: every
+// cache byte in range is read exactly once.
+//
+// Pass 1 (decode_split_kernel): the key range of each (item, kv head) is cut into
+// `splits` pieces, one workgroup each.  Every K/V row (head_dim bf16 = 256 bytes at
+// head_dim 128) is read by D/8 lanes with one 16-byte load each, so one wave load covers
+// 64 / (D/8) consecutive rows (1 KiB) -- fully coalesced.  The workgroup keeps the
+// queries of all GT query heads of the group in registers, so each K/V byte is read once
+// for the whole group (no per-query-head copy of the cache).  Dot products are reduced
+// across the lanes of a row with DPP, the softmax runs online in fp32, and the
+// workgroup's partial state (running max m, running sum l, unnormalised output o) is
+// written to the workspace.
+// Pass 2 (decode_combine_kernel): per (item, query head) the partial states of the
+// splits are merged exactly: m* = max m_s, out = sum_s 2^(m_s - m*) o_s / sum_s 2^(m_s - m*) l_s.
+#include "mi_attn_device.hpp"
+#include "mi_attn_kernels.hpp"
+
+namespace mi_attn {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kSteps = 8;   // wave loads per batch (rows per lane group between softmax updates)
+
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* base, size_t elem, float* x) {
+    if constexpr (BF16) {
+        const u32x4 w = *(const u32x4*)((const uint16_t*)base + elem);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = bf16_lo(w[i]);
+            x[2 * i + 1] = bf16_hi(w[i]);
+        }
+    } else {
+        const f32x4 a = *(const f32x4*)((const float*)base + elem);
+        const f32x4 b = *(const f32x4*)((const float*)base + elem + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = a[i];
+            x[4 + i] = b[i];
+        }
+    }
+}
+
+template <int D, int GT, bool BF16>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
+    constexpr int LPR = D / 8;            // lanes per key row, 8 elements per lane
+    constexpr int RPW = 64 / LPR;         // rows per wave load
+    constexpr int STREAMS = RPW * kWaves; // independent row streams in the workgroup
+    constexpr int BATCH = STREAMS * kSteps;
+
+    __shared__ float s_m[STREAMS][GT];
+    __shared__ float s_l[STREAMS][GT];
+    __shared__ float s_o[STREAMS][GT][D];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int r = lane / LPR, c = lane % LPR;
+    const int stream = wave * RPW + r;
+    const int b = blockIdx.z;
+    const int kvh = blockIdx.y / a.head_groups;
+    const int hg = blockIdx.y % a.head_groups;
+    const int split = blockIdx.x;
+    const int group = a.q_heads / a.kv_heads;
+    const int h0 = kvh * group + hg * GT;
+
+    // query position and the key interval [lo, hi] it sees
+    int len, pos;
+    if (a.kv_lens) {
+        len = min(max(a.kv_lens[b], 0), a.kv_len);
+        pos = len - 1;
+    } else {
+        len = a.kv_len;
+        pos = a.pos_offset;
+    }
+    const int lo = a.window > 0 ? max(0, pos - a.window + 1) : 0;
+    const int hi = min(pos, len - 1);
+    const int s0 = max(lo, split * a.split_len);
+    const int s1 = min(hi + 1, (split + 1) * a.split_len);
+
+    // queries of the GT heads, pre-multiplied by scale * log2(e)
+    const float c2 = a.scale * kLog2e;
+    float qf[GT][8];
+#pragma unroll
+    for (int t = 0; t < GT; ++t) {
+        load8<BF16>(a.q, ((size_t)b * a.q_heads + h0 + t) * D + c * 8, qf[t]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qf[t][i] *= c2;
+    }
+
+    float m[GT], l[GT], o[GT][8];
+#pragma unroll
+    for (int t = 0; t < GT; ++t) {
+        m[t] = kNegInf;
+        l[t] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[t][i] = 0.0f;
+    }
+
+    const size_t head_base = ((size_t)b * a.kv_heads + kvh) * (size_t)a.capacity * D;
+    for (int base = s0; base < s1; base += BATCH) {
+        int key[kSteps];
+        float kx[kSteps][8];
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) {
+            key[u] = base + (u * kWaves + wave) * RPW + r;
+            const int kr = key[u] < s1 ? key[u] : s0;     // out-of-range rows read a valid row
+            load8<BF16>(a.k, head_base + (size_t)kr * D + c * 8, kx[u]);
+        }
+        float s[kSteps][GT];
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) {
+#pragma unroll
+            for (int t = 0; t < GT; ++t) {
+                float d = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) d = fmaf(qf[t][i], kx[u][i], d);
+                d = row_sum<LPR>(d);
+                s[u][t] = key[u] < s1 ? d : kNegInf;
+            }
+        }
+        float vx[kSteps][8];
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) {
+            const int kr = key[u] < s1 ? key[u] : s0;
+            load8<BF16>(a.v, head_base + (size_t)kr * D + c * 8, vx[u]);
+        }
+#pragma unroll
+        for (int t = 0; t < GT; ++t) {
+            float mx = kNegInf;
+#pragma unroll
+            for (int u = 0; u < kSteps; ++u) mx = fmaxf(mx, s[u][t]);
+            const float m_new = fmaxf(m[t], mx);
+            const float m_use = m_new == kNegInf ? 0.0f : m_new;
+            const float alpha = fast_exp2(m[t] - m_use);
+            m[t] = m_new;
+            float ps = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[t][i] *= alpha;
+#pragma unroll
+            for (int u = 0; u < kSteps; ++u) {
+                const float p = fast_exp2(s[u][t] - m_use);
+                ps += p;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[t][i] = fmaf(p, vx[u][i], o[t][i]);
+            }
+            l[t] = l[t] * alpha + ps;
+        }
+    }
+
+    // merge the workgroup's row streams
+#pragma unroll
+    for (int t = 0; t < GT; ++t) {
+        if (c == 0) {
+            s_m[stream][t] = m[t];
+            s_l[stream][t] = l[t];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s_o[stream][t][c * 8 + i] = o[t][i];
+    }
+    __syncthreads();
+    for (int x = tid; x < GT * D; x += kThreads) {
+        const int t = x / D, d = x % D;
+        float mm = kNegInf;
+#pragma unroll
+        for (int st = 0; st < STREAMS; ++st) mm = fmaxf(mm, s_m[st][t]);
+        const float m_use = mm == kNegInf ? 0.0f : mm;
+        float acc = 0.0f, ll = 0.0f;
+#pragma unroll
+        for (int st = 0; st < STREAMS; ++st) {
+            const float w = fast_exp2(s_m[st][t] - m_use);
+            acc = fmaf(w, s_o[st][t][d], acc);
+            ll = fmaf(w, s_l[st][t], ll);
+        }
+        float* ws = a.ws + (((size_t)b * a.q_heads + h0 + t) * a.splits + split) * (D + 2);
+        ws[d] = acc;
+        if (d == 0) {
+            ws[D] = mm;
+            ws[D + 1] = ll;
+        }
+    }
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+    const int d = threadIdx.x;
+    const size_t bh = blockIdx.x;   // b * q_heads + h
+    const float* ws = a.ws + bh * a.splits * (D + 2);
+    float mm = kNegInf;
+    for (int s = 0; s < a.splits; ++s) mm = fmaxf(mm, ws[s * (D + 2) + D]);
+    const float m_use = mm == kNegInf ? 0.0f : mm;
+    float acc = 0.0f, ll = 0.0f;
+    for (int s = 0; s < a.splits; ++s) {
+        const float w = fast_exp2(ws[s * (D + 2) + D] - m_use);
+        acc = fmaf(w, ws[s * (D + 2) + d], acc);
+        ll = fmaf(w, ws[s * (D + 2) + D + 1], ll);
+    }
+    const float res = ll > 0.0f ? acc / ll : 0.0f;
+    if constexpr (BF16) {
+        ((__bf16*)a.out)[bh * D + d] = (__bf16)res;
+    } else {
+        ((float*)a.out)[bh * D + d] = res;
+    }
+}
+
+template <int D, bool BF16>
+hipError_t launch_d(const DecodeArgs& a, int gt, hipStream_t stream) {
+    dim3 grid(a.splits, a.kv_heads * a.head_groups, a.batch), block(kThreads);
+    switch (gt) {
+        case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1, BF16>), grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, BF16>), grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((decode_split_kernel<D, 4, BF16>), grid, block, 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((decode_split_kernel<D, 8, BF16>), grid, block, 0, stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_combine_kernel<D, BF16>), dim3(a.batch * a.q_heads), dim3(D), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int batch, int q_heads, int kv_heads, int kv_len, int head_dim) {
+    DecodePlan p{};
+    const int group = q_heads / kv_heads;
+    p.heads_per_group = group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+    p.head_groups = group / p.heads_per_group;
+    const long units = (long)batch * kv_heads * p.head_groups;
+    const long target_wgs = 2048;
+    long splits = (target_wgs + units - 1) / units;
+    const long max_splits = (kv_len + 255) / 256;
+    if (splits > max_splits) splits = max_splits;
+    if (splits < 1) splits = 1;
+    long split_len = (kv_len + splits - 1) / splits;
+    split_len = (split_len + 63) / 64 * 64;
+    splits = (kv_len + split_len - 1) / split_len;
+    p.splits = (int)splits;
+    p.split_len = (int)split_len;
+    (void)head_dim;
+    return p;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, int heads_per_group, bool bf16,
+                         hipStream_t stream) {
+    switch (head_dim) {
+        case 32: return bf16 ? launch_d<32, true>(a, heads_per_group, stream) : launch_d<32, false>(a, heads_per_group, stream);
+        case 64: return bf16 ? launch_d<64, true>(a, heads_per_group, stream) : launch_d<64, false>(a, heads_per_group, stream);
+        case 128: return bf16 ? launch_d<128, true>(a, heads_per_group, stream) : launch_d<128, false>(a, heads_per_group, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace mi_attn

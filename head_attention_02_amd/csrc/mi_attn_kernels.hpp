@@ -1,0 +1,50 @@
+// mi_attn_kernels.hpp -- kernel argument blocks and host-side launchers (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mi_attn {
+
+// One prefill problem, as validated by attn_prefill.
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    const int32_t* seq_lens;  // device [batch] or nullptr
+    int batch, q_heads, kv_heads, q_len, kv_len;
+    int pos_offset, window, causal;
+    float scale;
+    int n_qtiles;             // grid.x
+};
+
+// One decode problem, as validated and planned by attn_decode.
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* ws;                // [batch, q_heads, splits, head_dim + 2] partial states
+    const int32_t* kv_lens;   // device [batch] or nullptr
+    int batch, q_heads, kv_heads, kv_len, capacity;
+    int pos_offset, window;
+    float scale;
+    int splits, split_len;    // key-range split of each (item, kv head)
+    int head_groups;          // query-head groups per kv head (grid.y = kv_heads * head_groups)
+};
+
+// Each launcher enqueues on `stream` and returns the launch status.
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, int heads_per_group, bool bf16,
+                         hipStream_t stream);
+
+// Decode launch plan shared by the call and the workspace query.
+struct DecodePlan {
+    int splits, split_len, heads_per_group, head_groups;
+};
+DecodePlan plan_decode(int batch, int q_heads, int kv_heads, int kv_len, int head_dim);
+
+}  // namespace mi_attn

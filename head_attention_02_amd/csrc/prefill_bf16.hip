@@ -1,0 +1,307 @@
+// prefill_bf16.hip -- fused attention prefill for bf16 inputs on gfx950 matrix cores.
+//
+// Computes softmax(scale * Q K^T + mask) V per (item, query head) in one pass over the
+// keys, without materialising the score matrix: the scores of one key tile live in
+// registers, the row softmax is kept online in fp32 (running max and running sum,
+// older partial results rescaled when the max grows), and both products run on
+// 32x32x16 bf16 MFMA with fp32 accumulation.  The pages' backends compute the same
+// thing as two batched GEMMs around a materialised, masked softmax (ripvec-core
+// `Driver` page, `gemm_batched` + `fused_scale_mask_softmax`; realizar
+// `cached/attention.rs`, `single_dispatch_multihead_attention`); the banded variant
+// only visits keys inside the band (ripvec-core `Driver`, `banded_qk`), which here is
+// done by skipping whole key tiles.
+//
+// Work decomposition: one workgroup = 4 waves = 128 query rows of one (item, head);
+// wave w owns rows [32w, 32w+32).  Key tiles of 64 rows of K and V are staged in LDS
+// (16-byte chunks, XOR-swizzled per row) and shared by the 4 waves.
+//
+// Per wave and key tile:
+//   S^T (64 keys x 32 rows) = K_tile (A operand, from LDS) x Q^T (B operand, registers).
+//     With S^T instead of S, lane l holds scores of query row l%32 only, so the
+//     online softmax state (max, sum) of a row is private to lanes l and l^32.
+//   O^T (D x 32 rows) += V_tile^T (A operand) x P^T (B operand).
+//     P^T comes straight out of the S^T accumulator registers (converted to bf16);
+//     V^T is read from the row-major V tile with the transposing LDS read
+//     ds_read_b64_tr_b16, so V needs no transpose on its way into LDS.
+//   The key order inside each 16-key MFMA step is permuted identically on both
+//   operands (P from the accumulator layout, V by the LDS addresses), which leaves the
+//   contraction unchanged.
+#include "mi_attn_device.hpp"
+#include "mi_attn_kernels.hpp"
+
+namespace mi_attn {
+namespace {
+
+constexpr int kBM = 128;    // query rows per workgroup
+constexpr int kBN = 64;     // keys per tile
+constexpr int kThreads = 256;
+
+// XOR swizzle of the 16-byte chunk index within a row: spreads the 8 rows read by one
+// ds_read_b128 phase and the 4 rows of one transposing read over distinct banks.
+template <int CPR>
+__device__ __forceinline__ int swz(int row) {
+    return ((2 * row + (row >> 2)) & 7) & (CPR - 1);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a) {
+    constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
+    constexpr int KC = D / 16;                // MFMA k-steps of Q.K^T
+    constexpr int DB = D / 32;                // 32-wide blocks of the output head dim
+    constexpr int CPT = kBN * CPR / kThreads; // chunks per thread per tile (K and V each)
+    static_assert(CPT >= 1, "tile too small for the workgroup");
+
+    __shared__ __attribute__((aligned(16))) u32x4 k_lds[kBN * CPR];
+    __shared__ __attribute__((aligned(16))) u32x4 v_lds[kBN * CPR];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 5;                  // half of the wave
+    const int b = blockIdx.z;
+    const int h = blockIdx.y;
+    // causal tiles near the end of the sequence carry the most keys: launch them first
+    const int qt = a.causal ? (a.n_qtiles - 1 - (int)blockIdx.x) : (int)blockIdx.x;
+    const int kvh = h / (a.q_heads / a.kv_heads);
+
+    int valid = a.kv_len;
+    if (a.seq_lens) valid = min(max(a.seq_lens[b], 0), a.kv_len);
+
+    const int q0 = qt * kBM;
+    const int last_row = min(q0 + kBM, a.q_len) - 1;
+    const int half_w = a.window / 2;
+
+    // ---- key range of the whole workgroup -------------------------------------------
+    const int p_lo = a.pos_offset + q0;
+    const int p_hi = a.pos_offset + last_row;
+    int k_begin = 0;
+    int k_end = valid;
+    if (a.causal) k_end = min(k_end, p_hi + 1);
+    if (a.window > 0) {
+        if (a.causal) {
+            k_begin = max(k_begin, p_lo - a.window + 1);
+        } else {
+            k_begin = max(k_begin, p_lo - half_w);
+            k_end = min(k_end, p_hi + half_w + 1);
+        }
+    }
+    if (p_lo >= valid) k_end = k_begin;       // every row of the tile is padding
+    const int kt_begin = k_begin / kBN;
+    const int kt_end = k_end > k_begin ? (k_end + kBN - 1) / kBN : kt_begin;
+
+    // ---- this lane's query row and its key interval [lo_r, hi_r] ------------------------
+    const int my_row = q0 + wave * 32 + (lane & 31);
+    const int my_pos = a.pos_offset + my_row;
+    int lo_r = 0, hi_r = valid - 1;
+    if (a.causal) hi_r = min(hi_r, my_pos);
+    if (a.window > 0) {
+        if (a.causal) {
+            lo_r = max(0, my_pos - a.window + 1);
+        } else {
+            lo_r = max(0, my_pos - half_w);
+            hi_r = min(hi_r, my_pos + half_w);
+        }
+    }
+    if (my_pos >= valid || my_row >= a.q_len) hi_r = -1;
+
+    // the same for the wave as a whole (uniform): union and intersection of row intervals
+    const int w_row0 = q0 + wave * 32;
+    const int w_row1 = min(w_row0 + 31, a.q_len - 1);
+    const bool wave_live = w_row0 < a.q_len && a.pos_offset + w_row0 < valid;
+    const int wp_lo = a.pos_offset + w_row0, wp_hi = a.pos_offset + w_row1;
+    int w_union_lo = 0, w_union_hi = valid - 1, w_inter_lo = 0, w_inter_hi = valid - 1;
+    if (a.causal) {
+        w_union_hi = min(w_union_hi, wp_hi);
+        w_inter_hi = min(w_inter_hi, wp_lo);
+    }
+    if (a.window > 0) {
+        if (a.causal) {
+            w_union_lo = max(0, wp_lo - a.window + 1);
+            w_inter_lo = max(0, wp_hi - a.window + 1);
+        } else {
+            w_union_lo = max(0, wp_lo - half_w);
+            w_inter_lo = max(0, wp_hi - half_w);
+            w_union_hi = min(w_union_hi, wp_hi + half_w);
+            w_inter_hi = min(w_inter_hi, wp_lo + half_w);
+        }
+    }
+    const bool wave_all_rows_valid = wp_hi < valid;
+
+    // ---- Q^T operand: lane l holds row l%32, dims 16*kc + 8*g + [0, 8) ---------------
+    const size_t q_head = ((size_t)b * a.q_heads + h) * (size_t)a.q_len;
+    bf16x8 qf[KC];
+    {
+        const uint16_t* qrow = (const uint16_t*)a.q + (q_head + (size_t)min(my_row, a.q_len - 1)) * D;
+        const bool in = my_row < a.q_len;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            u32x4 w = in ? *(const u32x4*)(qrow + 16 * kc + 8 * g) : u32x4{0, 0, 0, 0};
+            qf[kc] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+
+    const size_t kv_head = ((size_t)b * a.kv_heads + kvh) * (size_t)a.kv_len;
+    const uint16_t* kg = (const uint16_t*)a.k + kv_head * D;
+    const uint16_t* vg = (const uint16_t*)a.v + kv_head * D;
+
+    // global -> registers for one tile; rows at or past `valid` are zero-filled so that
+    // padded (possibly non-finite) keys and values never reach the products
+    u32x4 kr[CPT], vr[CPT];
+    auto load_tile = [&](int kt) {
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int ci = tid + kThreads * u;
+            const int row = ci / CPR, c = ci % CPR;
+            const int j = kt * kBN + row;
+            if (j < valid) {
+                kr[u] = *(const u32x4*)(kg + (size_t)j * D + c * 8);
+                vr[u] = *(const u32x4*)(vg + (size_t)j * D + c * 8);
+            } else {
+                kr[u] = u32x4{0, 0, 0, 0};
+                vr[u] = u32x4{0, 0, 0, 0};
+            }
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int ci = tid + kThreads * u;
+            const int row = ci / CPR, c = ci % CPR;
+            const int idx = row * CPR + (c ^ swz<CPR>(row));
+            k_lds[idx] = kr[u];
+            v_lds[idx] = vr[u];
+        }
+    };
+
+    // ---- running state ----------------------------------------------------------------
+    f32x16 o[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) o[i] = f32x16{};
+    float m_run = kNegInf;    // running max of scaled log2 scores of this lane's row
+    float l_run = 0.0f;       // running sum over this lane's half of the keys
+    const float c2 = a.scale * kLog2e;
+
+    if (kt_begin < kt_end) load_tile(kt_begin);
+
+    for (int kt = kt_begin; kt < kt_end; ++kt) {
+        __syncthreads();      // previous tile fully consumed
+        store_tile();
+        __syncthreads();
+        if (kt + 1 < kt_end) load_tile(kt + 1);
+
+        const int kbase = kt * kBN;
+        if (!wave_live || kbase > w_union_hi || kbase + kBN - 1 < w_union_lo) continue;
+        const bool full = wave_all_rows_valid && kbase >= w_inter_lo && kbase + kBN - 1 <= w_inter_hi;
+
+        // S^T = K_tile . Q^T : two 32-key blocks
+        f32x16 s[2];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            s[kb2] = f32x16{};
+            const int row = kb2 * 32 + (lane & 31);
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const int c = 2 * kc + g;
+                const bf16x8 kf = __builtin_bit_cast(bf16x8, k_lds[row * CPR + (c ^ swz<CPR>(row))]);
+                s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kc], s[kb2], 0, 0, 0);
+            }
+        }
+
+        // scale to log2 units and mask: element e of block kb2 is key
+        // kbase + 32*kb2 + 8*(e/4) + 4*g + e%4 of row my_row
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float t = s[kb2][e] * c2;
+                if (!full) {
+                    const int j = kbase + 32 * kb2 + 8 * (e / 4) + 4 * g + (e % 4);
+                    t = (j >= lo_r && j <= hi_r) ? t : kNegInf;
+                }
+                s[kb2][e] = t;
+                mx = fmaxf(mx, t);
+            }
+        }
+        mx = fmaxf(mx, swap_halves(mx));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);
+        m_run = m_new;
+
+        // probabilities -> bf16 B operands; P chunk c4 (16 keys) = block c4/2, elements
+        // 8*(c4%2) + [0, 8)
+        bf16x8 pf[4];
+        float psum = 0.0f;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            u32x4 w;
+#pragma unroll
+            for (int jj = 0; jj < 8; jj += 2) {
+                const float p0 = fast_exp2(s[c4 / 2][8 * (c4 % 2) + jj] - m_use);
+                const float p1 = fast_exp2(s[c4 / 2][8 * (c4 % 2) + jj + 1] - m_use);
+                psum += p0 + p1;
+                w[jj / 2] = pack_bf16x2(p0, p1);
+            }
+            pf[c4] = __builtin_bit_cast(bf16x8, w);
+        }
+        l_run = l_run * alpha + psum;
+#pragma unroll
+        for (int i = 0; i < DB; ++i) o[i] *= alpha;
+
+        // O^T += V^T . P^T; V^T via transposing reads. Within 16-lane group G = lane/16,
+        // source lane s points at key 16*c4 + 4*g + s/4 (+8), dims 32*db + 16*(G%2) + 4*(s%4).
+        const int sl = lane & 15;
+        const int dhalf = (lane >> 4) & 1;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            const int r0 = 16 * c4 + 4 * g + (sl >> 2);
+            const int r1 = r0 + 8;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int col = 32 * db + 16 * dhalf + 4 * (sl & 3);
+                const int ch = col >> 3, sub = (col & 7) * 2;
+                const s16x4 lo = lds_read_tr16(v_lds, (r0 * CPR + (ch ^ swz<CPR>(r0))) * 16 + sub);
+                const s16x4 hi = lds_read_tr16(v_lds, (r1 * CPR + (ch ^ swz<CPR>(r1))) * 16 + sub);
+                typedef __attribute__((ext_vector_type(8))) short s16x8;
+                const s16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[c4], o[db],
+                                                               0, 0, 0);
+            }
+        }
+    }
+
+    // ---- epilogue: normalise, zero padded / empty rows, store bf16 --------------------
+    if (my_row >= a.q_len) return;
+    const float l_tot = l_run + swap_halves(l_run);
+    const float inv = (hi_r >= 0 && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
+    uint16_t* orow = (uint16_t*)a.out + (q_head + (size_t)my_row) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const int d = 32 * db + 8 * e4 + 4 * g;
+            u32x2 w;
+            w[0] = pack_bf16x2(o[db][4 * e4] * inv, o[db][4 * e4 + 1] * inv);
+            w[1] = pack_bf16x2(o[db][4 * e4 + 2] * inv, o[db][4 * e4 + 3] * inv);
+            *(u32x2*)(orow + d) = w;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, hipStream_t stream) {
+    PrefillArgs args = a;
+    args.n_qtiles = (a.q_len + kBM - 1) / kBM;
+    dim3 grid(args.n_qtiles, a.q_heads, a.batch), block(kThreads);
+    switch (head_dim) {
+        case 32: hipLaunchKernelGGL(prefill_bf16_kernel<32>, grid, block, 0, stream, args); break;
+        case 64: hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, block, 0, stream, args); break;
+        case 128: hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, block, 0, stream, args); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mi_attn

@@ -1,0 +1,140 @@
+// prefill_f32.hip -- attention prefill for fp32 inputs (the accuracy path).
+//
+// Same single-pass, online-softmax algorithm as the bf16 kernel, in plain fp32 on the
+// vector ALUs: each lane owns one query row (its q and its output accumulator live in
+// registers), key/value tiles are staged in LDS and read by every lane at the same
+// address (a broadcast).  Only the keys of the row's key set contribute; tiles outside
+// the union of the rows' key ranges are never loaded.
+#include "mi_attn_device.hpp"
+#include "mi_attn_kernels.hpp"
+
+namespace mi_attn {
+namespace {
+
+constexpr int kRows = 64;   // query rows per workgroup (one wave)
+constexpr int kKeys = 32;   // keys per LDS tile
+
+template <int D>
+__global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
+    __shared__ __attribute__((aligned(16))) float k_lds[kKeys * D];
+    __shared__ __attribute__((aligned(16))) float v_lds[kKeys * D];
+
+    const int lane = threadIdx.x;
+    const int b = blockIdx.z, h = blockIdx.y;
+    const int qt = a.causal ? (a.n_qtiles - 1 - (int)blockIdx.x) : (int)blockIdx.x;
+    const int kvh = h / (a.q_heads / a.kv_heads);
+
+    int valid = a.kv_len;
+    if (a.seq_lens) valid = min(max(a.seq_lens[b], 0), a.kv_len);
+
+    const int q0 = qt * kRows;
+    const int last_row = min(q0 + kRows, a.q_len) - 1;
+    const int half_w = a.window / 2;
+    const int p_lo = a.pos_offset + q0, p_hi = a.pos_offset + last_row;
+    int k_begin = 0, k_end = valid;
+    if (a.causal) k_end = min(k_end, p_hi + 1);
+    if (a.window > 0) {
+        if (a.causal) {
+            k_begin = max(k_begin, p_lo - a.window + 1);
+        } else {
+            k_begin = max(k_begin, p_lo - half_w);
+            k_end = min(k_end, p_hi + half_w + 1);
+        }
+    }
+    if (p_lo >= valid) k_end = k_begin;
+
+    const int row = q0 + lane;
+    const int pos = a.pos_offset + row;
+    int lo_r = 0, hi_r = valid - 1;
+    if (a.causal) hi_r = min(hi_r, pos);
+    if (a.window > 0) {
+        if (a.causal) {
+            lo_r = max(0, pos - a.window + 1);
+        } else {
+            lo_r = max(0, pos - half_w);
+            hi_r = min(hi_r, pos + half_w);
+        }
+    }
+    if (pos >= valid || row >= a.q_len) hi_r = -1;
+
+    const size_t q_head = ((size_t)b * a.q_heads + h) * (size_t)a.q_len;
+    const float* qrow = (const float*)a.q + (q_head + (size_t)min(row, a.q_len - 1)) * D;
+    float q[D], o[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        q[d] = row < a.q_len ? qrow[d] : 0.0f;
+        o[d] = 0.0f;
+    }
+    const size_t kv_head = ((size_t)b * a.kv_heads + kvh) * (size_t)a.kv_len;
+    const float* kg = (const float*)a.k + kv_head * D;
+    const float* vg = (const float*)a.v + kv_head * D;
+
+    float m_run = kNegInf, l_run = 0.0f;
+    const int t_begin = k_begin / kKeys;
+    const int t_end = k_end > k_begin ? (k_end + kKeys - 1) / kKeys : t_begin;
+    for (int t = t_begin; t < t_end; ++t) {
+        const int kbase = t * kKeys;
+        __syncthreads();
+        for (int x = lane; x < kKeys * D / 4; x += 64) {
+            const int r = x / (D / 4), c4 = x % (D / 4);
+            const int j = kbase + r;
+            f32x4 kk = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+            if (j < valid) {
+                kk = *(const f32x4*)(kg + (size_t)j * D + 4 * c4);
+                vv = *(const f32x4*)(vg + (size_t)j * D + 4 * c4);
+            }
+            *(f32x4*)(k_lds + r * D + 4 * c4) = kk;
+            *(f32x4*)(v_lds + r * D + 4 * c4) = vv;
+        }
+        __syncthreads();
+
+        float s[kKeys];
+        float mx = kNegInf;
+#pragma unroll
+        for (int jj = 0; jj < kKeys; ++jj) {
+            float dot = 0.0f;
+#pragma unroll
+            for (int d = 0; d < D; ++d) dot = fmaf(q[d], k_lds[jj * D + d], dot);
+            const int j = kbase + jj;
+            s[jj] = (j >= lo_r && j <= hi_r) ? dot * a.scale : kNegInf;
+            mx = fmaxf(mx, s[jj]);
+        }
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = m_new == kNegInf ? 0.0f : m_new;
+        const float alpha = expf(m_run - m_use);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < D; ++d) o[d] *= alpha;
+#pragma unroll
+        for (int jj = 0; jj < kKeys; ++jj) {
+            const float p = expf(s[jj] - m_use);
+            l_run += p;
+#pragma unroll
+            for (int d = 0; d < D; ++d) o[d] = fmaf(p, v_lds[jj * D + d], o[d]);
+        }
+    }
+
+    if (row >= a.q_len) return;
+    const float inv = (hi_r >= 0 && l_run > 0.0f) ? 1.0f / l_run : 0.0f;
+    float* orow = (float*)a.out + (q_head + (size_t)row) * D;
+#pragma unroll
+    for (int d = 0; d < D; d += 4) *(f32x4*)(orow + d) = f32x4{o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv};
+}
+
+}  // namespace
+
+hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, hipStream_t stream) {
+    PrefillArgs args = a;
+    args.n_qtiles = (a.q_len + kRows - 1) / kRows;
+    dim3 grid(args.n_qtiles, a.q_heads, a.batch), block(64);
+    switch (head_dim) {
+        case 32: hipLaunchKernelGGL(prefill_f32_kernel<32>, grid, block, 0, stream, args); break;
+        case 64: hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, block, 0, stream, args); break;
+        case 128: hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, block, 0, stream, args); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mi_attn

@@ -1,0 +1,137 @@
+/*
+ * mi_attn.h -- C ABI of libmi_attn: multi-head scaled-dot-product attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Two operations, both computing, for every batch item b, query head h and query
+ * row i,
+ *
+ *     out[b,h,i,:] = sum_{j in J} softmax_J(scale * q[b,h,i,:] . k[b,kh,j,:]) * v[b,kh,j,:]
+ *
+ * where kh = h / (q_heads / kv_heads) (contiguous groups of query heads share one
+ * K/V head) and J is the key set of the row (causal prefix, valid length, window).
+ * A row whose key set is empty, or whose query position lies at or past the item's
+ * valid length (a padded row), is written as zeros.
+ *
+ * Sources (docs.rs pages):
+ *   - ferrum-kernels 0.8.7, trait `Backend`, Required Methods: `flash_attention`
+ *     (q, k, v, out, batch, q_len, kv_len, pos_offset, config) -- the prefill call;
+ *     `qk_norm_rope` -- head-major [heads, tokens, head_dim] layout, token i at
+ *     position pos_offset + i; `kv_cache_append_head_major` -- cache layout
+ *     [kv_heads, capacity, head_dim]; `flash_attention_batched_per_cache` -- the
+ *     batched decode call: per-item kv_lens in a device buffer, scale, sliding_window
+ *     (0 = full causal, w > 0 = the last w valid positions).
+ *   - ripvec-core 0.8.3, trait `Driver`, Required Methods: `fused_scale_mask_softmax`
+ *     (softmax(scores * scale + mask) per head), `fused_scale_mask_softmax_windowed`
+ *     (|query_pos - key_pos| > window/2 masked), `build_attn_mask` (per-item key
+ *     padding), `unpad_from_batch` (padded rows are discarded).
+ *   - realizar 0.8.5, `src/gguf/inference/cached/attention.rs`:
+ *     `parallel_multihead_attention_gpu_cached` (scale 1/sqrt(head_dim) applied to
+ *     the scores before the softmax) and `batched_causal_softmax` (rows normalised
+ *     only when their exponential sum is positive).
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers to contiguous row-major arrays, 16-byte
+ *     aligned.  The caller owns every buffer; the library keeps no pointer after a call
+ *     returns and allocates no device memory.
+ *   - `dtype` is MI_ATTN_BF16 or MI_ATTN_F32 and applies to q, k, v and out alike.
+ *     bf16 inputs are multiplied on matrix cores with fp32 accumulation; the softmax
+ *     runs in fp32; bf16 outputs are rounded to nearest even.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue work and
+ *     never synchronise; errors raised while the kernels run surface at the caller's
+ *     next synchronisation of that stream.
+ *   - Return value: a mi_attn_status.  On failure nothing is enqueued and
+ *     attn_last_error() holds "<call>: <reason>" for the calling thread.
+ *   - head_dim must be 32, 64 or 128 (else MI_ATTN_ERR_UNSUPPORTED; there is no slow
+ *     fallback).
+ */
+#ifndef MI_ATTN_H
+#define MI_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MI_ATTN_VERSION 1
+
+typedef enum { MI_ATTN_F32 = 0, MI_ATTN_BF16 = 1 } mi_attn_dtype;
+
+typedef enum {
+    MI_ATTN_OK = 0,
+    MI_ATTN_ERR_INVALID = 1,     /* bad pointer, size, alignment, or relation between sizes */
+    MI_ATTN_ERR_UNSUPPORTED = 2, /* valid request this build does not implement            */
+    MI_ATTN_ERR_HIP = 3          /* the HIP runtime refused a launch                       */
+} mi_attn_status;
+
+/*
+ * attn_prefill -- attention of q_len query rows against kv_len keys per (item, head).
+ * Follows `flash_attention` of the ferrum-kernels `Backend` page, with the mask kinds
+ * of the ripvec-core `Driver` page.
+ *
+ *   q    [batch, q_heads,  q_len,  head_dim]
+ *   k, v [batch, kv_heads, kv_len, head_dim]
+ *   out  [batch, q_heads,  q_len,  head_dim]   written in full (padded rows = 0)
+ *   q_heads % kv_heads == 0; query head h reads K/V head h / (q_heads / kv_heads).
+ *   pos_offset  absolute position of query row 0 (row i sits at pos_offset + i; key j
+ *               at position j); requires pos_offset >= 0 and pos_offset + q_len <= kv_len.
+ *   seq_lens    NULL, or DEVICE int32 [batch]: valid key count of each item (values are
+ *               clamped to [0, kv_len]).  Keys j >= seq_lens[b] are ignored and query
+ *               rows at positions >= seq_lens[b] are padding (written as 0).  Values
+ *               past the valid length may be anything, NaN included.
+ *   window      0: no band.  causal != 0: a query at p sees keys p - window < j <= p.
+ *               causal == 0: a query at p sees keys with |p - j| <= window / 2.
+ *   causal      nonzero: keys j > p are masked.
+ *   scale       multiplies q.k before the softmax, used exactly as given (1/sqrt(head_dim)
+ *               is the usual value).
+ *   batch == 0 or q_len == 0 is a valid empty call (nothing is enqueued).
+ */
+int attn_prefill(const void* q, const void* k, const void* v, void* out, int batch, int q_heads,
+                 int kv_heads, int q_len, int kv_len, int head_dim, int pos_offset,
+                 const int32_t* seq_lens, int window, int causal, float scale, int dtype,
+                 void* stream);
+
+/*
+ * attn_decode -- one query token per (item, query head) against a head-major KV cache.
+ * Follows `flash_attention_batched_per_cache` and `kv_cache_append_head_major` of the
+ * ferrum-kernels `Backend` page, with the per-item caches stacked in one allocation.
+ *
+ *   q        [batch, q_heads, head_dim]
+ *   k_cache  [batch, kv_heads, capacity, head_dim]  slots [0, kv_len) hold keys
+ *   v_cache  [batch, kv_heads, capacity, head_dim]
+ *   out      [batch, q_heads, head_dim]
+ *   1 <= kv_len <= capacity.  Slots at or past an item's length are never read.
+ *   kv_lens  NULL: every item has kv_len keys and its query sits at pos_offset
+ *            (0 <= pos_offset < kv_len), seeing keys j <= pos_offset.
+ *            DEVICE int32 [batch]: item b has kv_lens[b] keys (clamped to [0, kv_len])
+ *            and its query sits at kv_lens[b] - 1 (pos_offset is then unused); an item
+ *            with no keys gets zeros.  kv_len is the largest length any item may have.
+ *   window   0: all causal keys; w > 0: only the last w positions p - w < j <= p.
+ *   workspace, workspace_bytes  DEVICE scratch of at least
+ *            attn_decode_workspace_bytes(batch, q_heads, kv_heads, kv_len, head_dim)
+ *            bytes, 256-byte aligned, not used by anything else until the call's
+ *            kernels finish (the call holds partial softmax states in it).
+ *   batch == 0 is a valid empty call.
+ */
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* out, int batch,
+                int q_heads, int kv_heads, int kv_len, int capacity, int head_dim, int pos_offset,
+                const int32_t* kv_lens, int window, float scale, int dtype, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* Scratch bytes attn_decode needs for these sizes (0 when it needs none).  Pure host
+ * function; returns 0 for sizes attn_decode would reject. */
+size_t attn_decode_workspace_bytes(int batch, int q_heads, int kv_heads, int kv_len, int head_dim);
+
+/* Message of the calling thread's last failed call ("" if none).  The pointer stays
+ * valid until that thread's next call into the library. */
+const char* attn_last_error(void);
+
+/* MI_ATTN_VERSION of the built library. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI_ATTN_H */

@@ -1,0 +1,112 @@
+"""libmi_attn on the CPU: it loads, exports every declared symbol, and its host-side
+validation rejects bad arguments before touching the GPU (no kernel is launched here)."""
+import ctypes
+import math
+import re
+from pathlib import Path
+
+import pytest
+
+import head_attention_02_amd as mi
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "mi_attn.h"
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(mi.EXPORTS)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = mi.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    version = int(re.search(r"#define MI_ATTN_VERSION (\d+)", HEADER.read_text()).group(1))
+    assert mi.attn_version() == version
+
+
+def test_workspace_query():
+    n = mi.attn_decode_workspace_bytes(64, 32, 8, 8192, 128)
+    assert n > 0 and n % 4 == 0
+    # one fp32 partial state (head_dim + 2 values) per (item, query head, split)
+    per_split = 64 * 32 * (128 + 2) * 4
+    assert n % per_split == 0
+    assert mi.attn_decode_workspace_bytes(0, 32, 8, 8192, 128) == 0
+    assert mi.attn_decode_workspace_bytes(64, 30, 8, 8192, 128) == 0
+    assert mi.attn_decode_workspace_bytes(64, 32, 8, 8192, 96) == 0
+
+
+FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: validation fails first
+
+
+def prefill(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, batch=2, q_heads=8, kv_heads=2, q_len=16, kv_len=16,
+                head_dim=64, pos_offset=0, seq_lens=None, window=0, causal=1, scale=0.125, dtype=mi.MI_ATTN_BF16,
+                stream=None)
+    args.update(kw)
+    return mi.library().attn_prefill(*args.values())
+
+
+def decode(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, batch=2, q_heads=8, kv_heads=2, kv_len=16, capacity=16,
+                head_dim=64, pos_offset=15, kv_lens=None, window=0, scale=0.125, dtype=mi.MI_ATTN_BF16,
+                ws=FAKE, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return mi.library().attn_decode(*args.values())
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(q_heads=6, kv_heads=4), mi.MI_ATTN_ERR_INVALID, "not a multiple"),
+    (dict(kv_heads=0), mi.MI_ATTN_ERR_INVALID, "must be >= 1"),
+    (dict(pos_offset=4), mi.MI_ATTN_ERR_INVALID, "exceeds kv_len"),
+    (dict(pos_offset=-1), mi.MI_ATTN_ERR_INVALID, "exceeds kv_len"),
+    (dict(q_len=-1), mi.MI_ATTN_ERR_INVALID, "negative size"),
+    (dict(window=-3), mi.MI_ATTN_ERR_INVALID, "negative"),
+    (dict(scale=math.inf), mi.MI_ATTN_ERR_INVALID, "not finite"),
+    (dict(head_dim=96), mi.MI_ATTN_ERR_UNSUPPORTED, "head_dim 96"),
+    (dict(dtype=7), mi.MI_ATTN_ERR_UNSUPPORTED, "dtype"),
+    (dict(q=None), mi.MI_ATTN_ERR_INVALID, "null"),
+    (dict(out=ctypes.c_void_p(0x100004)), mi.MI_ATTN_ERR_INVALID, "aligned"),
+])
+def test_prefill_validation(kw, status, msg):
+    assert prefill(**kw) == status
+    err = mi.attn_last_error()
+    assert err.startswith("attn_prefill: ") and msg in err
+
+
+def test_prefill_empty_calls_are_ok_without_a_gpu():
+    assert prefill(batch=0) == mi.MI_ATTN_OK
+    assert prefill(q_len=0, q=None) == mi.MI_ATTN_OK
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(q_heads=6, kv_heads=4), mi.MI_ATTN_ERR_INVALID, "not a multiple"),
+    (dict(kv_len=17), mi.MI_ATTN_ERR_INVALID, "capacity"),
+    (dict(kv_len=0), mi.MI_ATTN_ERR_INVALID, "capacity"),
+    (dict(pos_offset=16), mi.MI_ATTN_ERR_INVALID, "pos_offset"),
+    (dict(window=-1), mi.MI_ATTN_ERR_INVALID, "negative"),
+    (dict(head_dim=48), mi.MI_ATTN_ERR_UNSUPPORTED, "head_dim 48"),
+    (dict(ws_bytes=16), mi.MI_ATTN_ERR_INVALID, "workspace"),
+    (dict(ws=None), mi.MI_ATTN_ERR_INVALID, "workspace"),
+    (dict(v=None), mi.MI_ATTN_ERR_INVALID, "null"),
+])
+def test_decode_validation(kw, status, msg):
+    assert decode(**kw) == status
+    err = mi.attn_last_error()
+    assert err.startswith("attn_decode: ") and msg in err
+
+
+def test_decode_empty_batch_is_ok_without_a_gpu():
+    assert decode(batch=0) == mi.MI_ATTN_OK
+
+
+def test_error_message_is_cleared_by_a_good_call():
+    assert prefill(kv_heads=3) != mi.MI_ATTN_OK
+    assert mi.attn_last_error()
+    assert prefill(batch=0) == mi.MI_ATTN_OK
+    assert mi.attn_last_error() == ""

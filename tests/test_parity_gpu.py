@@ -1,0 +1,225 @@
+"""GPU parity: libmi_attn (through its C ABI) against the fp64 oracle, element by element.
+
+Sizes span several tiles with ragged tails; the five named workloads run at full size
+in the launch configuration the benchmark times (rows sampled where the oracle would
+take too long).  bf16: |gpu - ref| <= 2e-2 + 1e-2 |ref| elementwise; fp32: max abs 1e-4.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import check, to_f64, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mi():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the GPU tests need an MI355X")
+    import head_attention_02_amd as m
+    m.library()
+    return m
+
+
+@pytest.fixture(scope="module")
+def ref():
+    return oracle.default()
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def poison(arrays, lens, axis_len_dim, dtype):
+    """Write NaN into every position at or past each item's length (dim 2)."""
+    nan = W.BF16_NAN if dtype == "bf16" else np.float32(np.nan)
+    for a in arrays:
+        for b, n in enumerate(lens):
+            a[b, :, max(int(n), 0):] = nan
+
+
+# ---------------------------------------------------------------------------
+# prefill: assorted shapes
+
+PREFILL_CASES = [
+    # B, Hq, Hkv, Lq, Lk, D, causal, P, seq_lens, W, dtype
+    (2, 4, 4, 300, 300, 64, False, 0, None, 0, "bf16"),
+    (1, 8, 2, 257, 257, 128, True, 0, None, 0, "bf16"),
+    (2, 4, 1, 129, 400, 128, True, 271, None, 0, "bf16"),
+    (3, 6, 3, 200, 200, 32, False, 0, [200, 1, 0], 0, "bf16"),
+    (2, 4, 4, 333, 333, 64, False, 0, None, 128, "bf16"),
+    (1, 4, 4, 300, 300, 64, False, 0, None, 7, "bf16"),
+    (1, 8, 1, 190, 190, 128, True, 0, None, 50, "bf16"),
+    (2, 2, 2, 100, 150, 64, True, 50, [150, 120], 0, "bf16"),
+    (4, 4, 2, 64, 64, 128, False, 0, [64, 37, 1, 999], 0, "bf16"),
+    (1, 2, 2, 1, 1, 64, True, 0, None, 0, "bf16"),
+    (1, 16, 2, 130, 130, 32, True, 0, [97], 33, "bf16"),
+    (2, 4, 2, 150, 150, 64, True, 0, None, 0, "f32"),
+    (1, 2, 2, 70, 90, 128, False, 20, [85], 9, "f32"),
+    (1, 4, 4, 100, 100, 32, True, 0, None, 16, "f32"),
+    (3, 3, 1, 65, 65, 128, False, 0, [65, 0, 13], 0, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: "x".join(map(str, c[:6])) + f"-c{int(c[6])}-P{c[7]}-W{c[9]}-{c[10]}")
+def test_prefill_parity(mi, ref, case):
+    B, Hq, Hkv, Lq, Lk, D, causal, P, sl, Wn, dt = case
+    say(f"prefill case {case}")
+    x = W.random_prefill(7, B, Hq, Hkv, Lq, Lk, D, dt)
+    q, k, v = x["q"], x["k"], x["v"]
+    seq = None if sl is None else np.array(sl, np.int32)
+    if seq is not None:
+        poison([k, v], np.minimum(seq, Lk), 2, dt)
+        poison([q], np.clip(seq - P, 0, Lq), 2, dt)
+    scale = 1.0 / math.sqrt(D)
+    want = ref.prefill(q, k, v, scale=scale, causal=causal, pos_offset=P, seq_lens=seq, window=Wn)
+    got = mi.attn_prefill(to_gpu(q), to_gpu(k), to_gpu(v), pos_offset=P,
+                          seq_lens=None if seq is None else to_gpu(seq), window=Wn, causal=causal, scale=scale)
+    import torch
+    torch.cuda.synchronize()
+    g = to_f64(got)
+    if seq is not None:
+        for b in range(B):
+            pad_from = max(0, min(int(seq[b]), Lk) - P)
+            assert np.all(g[b, :, pad_from:] == 0.0), "padded query rows must be zero"
+    check(g, want, dt, f"prefill {case}")
+
+
+# ---------------------------------------------------------------------------
+# decode: assorted shapes
+
+DECODE_CASES = [
+    # B, Hq, Hkv, cap, kv_len, D, P, kv_lens, W, dtype
+    (4, 32, 8, 1024, 1000, 128, 999, None, 0, "bf16"),
+    (5, 8, 8, 700, 700, 64, 300, None, 0, "bf16"),
+    (6, 16, 2, 2048, 2000, 128, 0, [2000, 1, 0, 1500, 1999, 777], 0, "bf16"),
+    (3, 12, 4, 512, 512, 32, 0, [512, 100, 3], 64, "bf16"),
+    (2, 8, 1, 333, 333, 128, 332, None, 1, "bf16"),
+    (2, 4, 1, 300, 300, 128, 299, None, 17, "f32"),
+    (2, 6, 2, 256, 200, 64, 0, [200, 50], 0, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: "x".join(map(str, c[:6])) + f"-P{c[6]}-W{c[8]}-{c[9]}")
+def test_decode_parity(mi, ref, case):
+    B, Hq, Hkv, cap, L, D, P, kl, Wn, dt = case
+    say(f"decode case {case}")
+    x = W.random_decode(11, B, Hq, Hkv, cap, D, dt)
+    q, k, v = x["q"], x["k"], x["v"]
+    lens = np.array(kl, np.int32) if kl is not None else None
+    poison([k, v], lens if lens is not None else [L] * B, 2, dt)
+    scale = 1.0 / math.sqrt(D)
+    want = ref.decode(q, k, v, kv_len=L, scale=scale, pos_offset=P, kv_lens=lens, window=Wn)
+    got = mi.attn_decode(to_gpu(q), to_gpu(k), to_gpu(v), kv_len=L, pos_offset=P,
+                         kv_lens=None if lens is None else to_gpu(lens), window=Wn, scale=scale)
+    import torch
+    torch.cuda.synchronize()
+    check(to_f64(got), want, dt, f"decode {case}")
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+
+def test_empty_calls(mi):
+    import torch
+    q = torch.empty((0, 4, 16, 64), dtype=torch.bfloat16, device="cuda")
+    assert mi.attn_prefill(q, q, q).shape == q.shape
+    q = torch.empty((2, 4, 0, 64), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((2, 4, 0, 64), dtype=torch.bfloat16, device="cuda")
+    assert mi.attn_prefill(q, k, k).numel() == 0
+    qd = torch.empty((0, 4, 64), dtype=torch.bfloat16, device="cuda")
+    kc = torch.empty((0, 4, 16, 64), dtype=torch.bfloat16, device="cuda")
+    assert mi.attn_decode(qd, kc, kc).numel() == 0
+
+
+def test_decode_all_items_empty(mi):
+    import torch
+    x = W.random_decode(3, 3, 8, 2, 64, 128, "bf16")
+    lens = torch.zeros(3, dtype=torch.int32, device="cuda")
+    out = mi.attn_decode(to_gpu(x["q"]), to_gpu(x["k"]), to_gpu(x["v"]), kv_len=64, kv_lens=lens)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
+
+
+def test_prefill_writes_only_its_output(mi, ref):
+    """A canary after `out` in the same allocation stays untouched."""
+    import torch
+    x = W.random_prefill(5, 1, 4, 2, 200, 200, 128, "bf16")
+    n = 1 * 4 * 200 * 128
+    buf = torch.full((n + 4096,), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[:n].view(1, 4, 200, 128)
+    mi.attn_prefill(to_gpu(x["q"]), to_gpu(x["k"]), to_gpu(x["v"]), out, causal=True)
+    torch.cuda.synchronize()
+    assert torch.all(buf[n:] == 7.0)
+    want = ref.prefill(x["q"], x["k"], x["v"], scale=1 / math.sqrt(128), causal=True)
+    check(to_f64(out), want, "bf16", "canary run")
+
+
+def test_repeat_runs_are_bitwise_identical(mi):
+    import torch
+    x = W.random_prefill(9, 1, 8, 2, 512, 512, 128, "bf16")
+    q, k, v = to_gpu(x["q"]), to_gpu(x["k"]), to_gpu(x["v"])
+    a = mi.attn_prefill(q, k, v, causal=True).clone()
+    b = mi.attn_prefill(q, k, v, causal=True).clone()
+    xd = W.random_decode(9, 8, 32, 8, 4096, 128, "bf16")
+    qd, kd, vd = to_gpu(xd["q"]), to_gpu(xd["k"]), to_gpu(xd["v"])
+    c = mi.attn_decode(qd, kd, vd).clone()
+    d = mi.attn_decode(qd, kd, vd).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(c.view(torch.int16), d.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# the five named workloads at full size
+
+
+def _sample_rows(rng, B, H, L, n_random, edges):
+    rows = {(int(b), int(h), int(i)) for b, h, i in zip(rng.integers(0, B, n_random), rng.integers(0, H, n_random),
+                                                        rng.integers(0, L, n_random))}
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        for i in list(range(min(edges, L))) + list(range(max(0, L - edges), L)):
+            rows.add((b, h, i))
+    return np.array(sorted(rows), np.int32)
+
+
+@pytest.mark.parametrize("name", ["tiny_causal_f32", "bert_base_padded", "banded_w128_s8192", "causal_gqa_s4096"])
+def test_named_prefill_workload(mi, ref, name):
+    import torch
+    w = W.WORKLOADS[name]
+    say(f"workload {name}")
+    x = W.make_inputs(w)
+    seq = x["seq_lens"]
+    got = mi.attn_prefill(to_gpu(x["q"]), to_gpu(x["k"]), to_gpu(x["v"]), pos_offset=w.pos_offset,
+                          seq_lens=None if seq is None else to_gpu(seq), window=w.window, causal=w.causal,
+                          scale=w.attn_scale)
+    torch.cuda.synchronize()
+    g = to_f64(got)
+    kw = dict(scale=w.attn_scale, causal=w.causal, pos_offset=w.pos_offset, seq_lens=seq, window=w.window)
+    if name in ("tiny_causal_f32", "bert_base_padded"):
+        want = ref.prefill(x["q"], x["k"], x["v"], **kw)
+        check(g, want, w.dtype, name)
+    else:
+        rows = _sample_rows(np.random.default_rng(0), w.batch, w.q_heads, w.q_len, 2000, 140)
+        want = ref.prefill(x["q"], x["k"], x["v"], rows=rows, **kw)
+        check(g[rows[:, 0], rows[:, 1], rows[:, 2]], want, w.dtype, name)
+
+
+def test_named_decode_workload(mi, ref):
+    import torch
+    w = W.WORKLOADS["gqa_decode_kv8192"]
+    say("workload gqa_decode_kv8192")
+    x = W.make_inputs(w)
+    got = mi.attn_decode(to_gpu(x["q"]), to_gpu(x["k"]), to_gpu(x["v"]), kv_len=w.kv_len, pos_offset=w.pos_offset,
+                         window=w.window, scale=w.attn_scale)
+    torch.cuda.synchronize()
+    want = ref.decode(x["q"], x["k"], x["v"], kv_len=w.kv_len, scale=w.attn_scale, pos_offset=w.pos_offset,
+                      window=w.window)
+    check(to_f64(got), want, w.dtype, "gqa_decode_kv8192")
