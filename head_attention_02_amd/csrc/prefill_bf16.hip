@@ -3,29 +3,38 @@
 // Computes softmax(scale * Q K^T + mask) V per (item, query head) in one pass over the
 // keys, without materialising the score matrix: the scores of one key tile live in
 // registers, the row softmax is kept online in fp32 (running max and running sum,
-// older partial results rescaled when the max grows), and both products run on
-// 32x32x16 bf16 MFMA with fp32 accumulation.  The pages' backends compute the same
-// thing as two batched GEMMs around a materialised, masked softmax (ripvec-core
-// `Driver` page, `gemm_batched` + `fused_scale_mask_softmax`; realizar
-// `cached/attention.rs`, `single_dispatch_multihead_attention`); the banded variant
-// only visits keys inside the band (ripvec-core `Driver`, `banded_qk`), which here is
-// done by skipping whole key tiles.
+// partial results rescaled when the max grows), and both products run on 32x32x16
+// bf16 MFMA with fp32 accumulation.  The pages' backends compute the same thing as two
+// batched GEMMs around a materialised, masked softmax (ripvec-core `Driver` page,
+// `gemm_batched` + `fused_scale_mask_softmax`; realizar `cached/attention.rs`,
+// `single_dispatch_multihead_attention`); the banded variant only visits keys inside
+// the band (ripvec-core `Driver`, `banded_qk`), which here is done by skipping whole
+// key tiles.
 //
 // Work decomposition: one workgroup = 4 waves = 128 query rows of one (item, head);
-// wave w owns rows [32w, 32w+32).  Key tiles of 64 rows of K and V are staged in LDS
-// (16-byte chunks, XOR-swizzled per row) and shared by the 4 waves.
+// wave w owns rows [32w, 32w+32).  Key tiles of 64 rows of K and V are copied from HBM
+// straight into LDS (global_load_lds_dwordx4, 16 bytes per lane, no registers), double
+// buffered so that the copy of tile t+1 overlaps the math on tile t, with one barrier
+// per tile.  16-byte chunks are XOR-swizzled per row (the swizzle is applied on the
+// global side: each lane fetches the chunk that belongs at its LDS slot).
 //
 // Per wave and key tile:
 //   S^T (64 keys x 32 rows) = K_tile (A operand, from LDS) x Q^T (B operand, registers).
 //     With S^T instead of S, lane l holds scores of query row l%32 only, so the
 //     online softmax state (max, sum) of a row is private to lanes l and l^32.
 //   O^T (D x 32 rows) += V_tile^T (A operand) x P^T (B operand).
-//     P^T comes straight out of the S^T accumulator registers (converted to bf16);
+//     P^T comes straight out of the S^T accumulator registers (packed to bf16);
 //     V^T is read from the row-major V tile with the transposing LDS read
 //     ds_read_b64_tr_b16, so V needs no transpose on its way into LDS.
 //   The key order inside each 16-key MFMA step is permuted identically on both
 //   operands (P from the accumulator layout, V by the LDS addresses), which leaves the
 //   contraction unchanged.
+//
+// Softmax bookkeeping per tile, for scale > 0: the max is taken over raw scores and the
+// scale is folded into one FMA per score, p = exp2(s*c - m*c) with c = scale*log2(e).
+// The running max is only moved (and O, l rescaled) when the tile's max exceeds it by
+// more than 2^8; otherwise the stale max is kept, p <= 256, and the final O / l is
+// unchanged because numerator and denominator share it.
 #include "mi_attn_device.hpp"
 #include "mi_attn_kernels.hpp"
 
@@ -35,6 +44,7 @@ namespace {
 constexpr int kBM = 128;    // query rows per workgroup
 constexpr int kBN = 64;     // keys per tile
 constexpr int kThreads = 256;
+constexpr float kRescaleSlack = 8.0f;  // log2 units the stale max may lag behind
 
 // XOR swizzle of the 16-byte chunk index within a row: spreads the 8 rows read by one
 // ds_read_b128 phase and the 4 rows of one transposing read over distinct banks.
@@ -43,16 +53,47 @@ __device__ __forceinline__ int swz(int row) {
     return ((2 * row + (row >> 2)) & 7) & (CPR - 1);
 }
 
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// Row max over both halves of the wave (lanes l and l^32 hold the same query row).
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Copy key tile `kt` of K and V (rows clamped to valid-1: rows past the valid length
+// hold finite copies of a valid row and are masked out of the softmax) into LDS.
 template <int D>
+__device__ __forceinline__ void tile_to_lds(u32x4* k_dst, u32x4* v_dst, const uint16_t* kg, const uint16_t* vg,
+                                            int kt, int valid, int wave, int lane) {
+    constexpr int CPR = D / 8;
+    constexpr int CPT = kBN * CPR / kThreads;
+    typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+        const int slot0 = (u * (kThreads / 64) + wave) * 64;   // wave-uniform LDS slot base
+        const int p = slot0 + lane;
+        const int row = p / CPR;
+        const int c = (p % CPR) ^ swz<CPR>(row);
+        const int j = min(kt * kBN + row, valid - 1);
+        const size_t off = (size_t)j * D + c * 8;
+        __builtin_amdgcn_global_load_lds((const void*)(kg + off), (lds_void*)(k_dst + slot0), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vg + off), (lds_void*)(v_dst + slot0), 16, 0, 0);
+    }
+}
+
+template <int D, bool POS_SCALE>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a) {
     constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
     constexpr int KC = D / 16;                // MFMA k-steps of Q.K^T
     constexpr int DB = D / 32;                // 32-wide blocks of the output head dim
-    constexpr int CPT = kBN * CPR / kThreads; // chunks per thread per tile (K and V each)
-    static_assert(CPT >= 1, "tile too small for the workgroup");
+    constexpr int TILE = kBN * CPR;           // 16-byte chunks per K (or V) tile
 
-    __shared__ __attribute__((aligned(16))) u32x4 k_lds[kBN * CPR];
-    __shared__ __attribute__((aligned(16))) u32x4 v_lds[kBN * CPR];
+    __shared__ __attribute__((aligned(16))) u32x4 lds[2][2][TILE];   // [buffer][K or V][chunk]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -144,54 +185,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     const uint16_t* kg = (const uint16_t*)a.k + kv_head * D;
     const uint16_t* vg = (const uint16_t*)a.v + kv_head * D;
 
-    // global -> registers for one tile; rows at or past `valid` are zero-filled so that
-    // padded (possibly non-finite) keys and values never reach the products
-    u32x4 kr[CPT], vr[CPT];
-    auto load_tile = [&](int kt) {
-#pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            const int ci = tid + kThreads * u;
-            const int row = ci / CPR, c = ci % CPR;
-            const int j = kt * kBN + row;
-            if (j < valid) {
-                kr[u] = *(const u32x4*)(kg + (size_t)j * D + c * 8);
-                vr[u] = *(const u32x4*)(vg + (size_t)j * D + c * 8);
-            } else {
-                kr[u] = u32x4{0, 0, 0, 0};
-                vr[u] = u32x4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            const int ci = tid + kThreads * u;
-            const int row = ci / CPR, c = ci % CPR;
-            const int idx = row * CPR + (c ^ swz<CPR>(row));
-            k_lds[idx] = kr[u];
-            v_lds[idx] = vr[u];
-        }
-    };
-
     // ---- running state ----------------------------------------------------------------
     f32x16 o[DB];
 #pragma unroll
     for (int i = 0; i < DB; ++i) o[i] = f32x16{};
-    float m_run = kNegInf;    // running max of scaled log2 scores of this lane's row
+    float m_run = kNegInf;    // running (possibly stale) max of this lane's row, log2 units
     float l_run = 0.0f;       // running sum over this lane's half of the keys
     const float c2 = a.scale * kLog2e;
 
-    if (kt_begin < kt_end) load_tile(kt_begin);
+    if (kt_begin < kt_end) tile_to_lds<D>(lds[0][0], lds[0][1], kg, vg, kt_begin, valid, wave, lane);
 
     for (int kt = kt_begin; kt < kt_end; ++kt) {
-        __syncthreads();      // previous tile fully consumed
-        store_tile();
-        __syncthreads();
-        if (kt + 1 < kt_end) load_tile(kt + 1);
+        const int buf = (kt - kt_begin) & 1;
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's copies of tile kt landed
+        __syncthreads();                        // ... everyone's; and tile kt-1 is no longer read
+        if (kt + 1 < kt_end) tile_to_lds<D>(lds[buf ^ 1][0], lds[buf ^ 1][1], kg, vg, kt + 1, valid, wave, lane);
 
         const int kbase = kt * kBN;
         if (!wave_live || kbase > w_union_hi || kbase + kBN - 1 < w_union_lo) continue;
         const bool full = wave_all_rows_valid && kbase >= w_inter_lo && kbase + kBN - 1 <= w_inter_hi;
+        const u32x4* k_t = lds[buf][0];
 
         // S^T = K_tile . Q^T : two 32-key blocks
         f32x16 s[2];
@@ -202,57 +215,76 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 const int c = 2 * kc + g;
-                const bf16x8 kf = __builtin_bit_cast(bf16x8, k_lds[row * CPR + (c ^ swz<CPR>(row))]);
+                const bf16x8 kf = __builtin_bit_cast(bf16x8, k_t[row * CPR + (c ^ swz<CPR>(row))]);
                 s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kc], s[kb2], 0, 0, 0);
             }
         }
 
-        // scale to log2 units and mask: element e of block kb2 is key
-        // kbase + 32*kb2 + 8*(e/4) + 4*g + e%4 of row my_row
+        // mask: element e of block kb2 is key kbase + 32*kb2 + 8*(e/4) + 4*g + e%4
+        if (!full) {
+            const int lo = lo_r - kbase - 4 * g, hi = hi_r - kbase - 4 * g;
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int jj = 32 * kb2 + 8 * (e / 4) + (e % 4);
+                    if (!POS_SCALE) s[kb2][e] *= c2;
+                    s[kb2][e] = (jj >= lo && jj <= hi) ? s[kb2][e] : kNegInf;
+                }
+        } else if (!POS_SCALE) {
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] *= c2;
+        }
+
+        // tile row max (raw scores when scale > 0, scaled scores otherwise)
         float mx = kNegInf;
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
+        for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float t = s[kb2][e] * c2;
-                if (!full) {
-                    const int j = kbase + 32 * kb2 + 8 * (e / 4) + 4 * g + (e % 4);
-                    t = (j >= lo_r && j <= hi_r) ? t : kNegInf;
-                }
-                s[kb2][e] = t;
-                mx = fmaxf(mx, t);
-            }
-        }
-        mx = fmaxf(mx, swap_halves(mx));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        m_run = m_new;
+            for (int e = 0; e < 16; e += 2) mx = max3(mx, s[kb2][e], s[kb2][e + 1]);
+        mx = halves_max(mx);
+        const float m_tile = POS_SCALE ? mx * c2 : mx;
 
-        // probabilities -> bf16 B operands; P chunk c4 (16 keys) = block c4/2, elements
-        // 8*(c4%2) + [0, 8)
+        // lazy rescale: move the running max only when the tile's max runs ahead of it
+        const bool need = m_tile > m_run + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            const float alpha = need ? fast_exp2(m_run - m_tile) : 1.0f;
+            m_run = need ? m_tile : m_run;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < DB; ++i) o[i] *= alpha;
+        }
+        const float m_use = m_run == kNegInf ? 0.0f : m_run;
+
+        // probabilities -> packed bf16 B operands; P chunk c4 (16 keys) = block c4/2,
+        // elements 8*(c4%2) + [0, 8).
         bf16x8 pf[4];
-        float psum = 0.0f;
+        float lsum0 = 0.0f, lsum1 = 0.0f;
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
             u32x4 w;
 #pragma unroll
             for (int jj = 0; jj < 8; jj += 2) {
-                const float p0 = fast_exp2(s[c4 / 2][8 * (c4 % 2) + jj] - m_use);
-                const float p1 = fast_exp2(s[c4 / 2][8 * (c4 % 2) + jj + 1] - m_use);
-                psum += p0 + p1;
+                float p0, p1;
+                if (POS_SCALE) {
+                    p0 = fast_exp2(fmaf(s[c4 / 2][8 * (c4 % 2) + jj], c2, -m_use));
+                    p1 = fast_exp2(fmaf(s[c4 / 2][8 * (c4 % 2) + jj + 1], c2, -m_use));
+                } else {
+                    p0 = fast_exp2(s[c4 / 2][8 * (c4 % 2) + jj] - m_use);
+                    p1 = fast_exp2(s[c4 / 2][8 * (c4 % 2) + jj + 1] - m_use);
+                }
                 w[jj / 2] = pack_bf16x2(p0, p1);
+                lsum0 += p0; lsum1 += p1;
             }
             pf[c4] = __builtin_bit_cast(bf16x8, w);
         }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int i = 0; i < DB; ++i) o[i] *= alpha;
+        l_run += lsum0 + lsum1;
 
         // O^T += V^T . P^T; V^T via transposing reads. Within 16-lane group G = lane/16,
         // source lane s points at key 16*c4 + 4*g + s/4 (+8), dims 32*db + 16*(G%2) + 4*(s%4).
         const int sl = lane & 15;
         const int dhalf = (lane >> 4) & 1;
+        void* v_t = (void*)lds[buf][1];
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
             const int r0 = 16 * c4 + 4 * g + (sl >> 2);
@@ -261,8 +293,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
             for (int db = 0; db < DB; ++db) {
                 const int col = 32 * db + 16 * dhalf + 4 * (sl & 3);
                 const int ch = col >> 3, sub = (col & 7) * 2;
-                const s16x4 lo = lds_read_tr16(v_lds, (r0 * CPR + (ch ^ swz<CPR>(r0))) * 16 + sub);
-                const s16x4 hi = lds_read_tr16(v_lds, (r1 * CPR + (ch ^ swz<CPR>(r1))) * 16 + sub);
+                const s16x4 lo = lds_read_tr16(v_t, (r0 * CPR + (ch ^ swz<CPR>(r0))) * 16 + sub);
+                const s16x4 hi = lds_read_tr16(v_t, (r1 * CPR + (ch ^ swz<CPR>(r1))) * 16 + sub);
                 typedef __attribute__((ext_vector_type(8))) short s16x8;
                 const s16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[c4], o[db],
@@ -272,8 +304,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     }
 
     // ---- epilogue: normalise, zero padded / empty rows, store bf16 --------------------
+    const float l_tot = halves_sum(l_run);
     if (my_row >= a.q_len) return;
-    const float l_tot = l_run + swap_halves(l_run);
     const float inv = (hi_r >= 0 && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
     uint16_t* orow = (uint16_t*)a.out + (q_head + (size_t)my_row) * D;
 #pragma unroll
@@ -289,19 +321,27 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     }
 }
 
+template <int D>
+hipError_t launch_d(const PrefillArgs& args, dim3 grid, hipStream_t stream) {
+    if (args.scale > 0.0f)
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, true>), grid, dim3(kThreads), 0, stream, args);
+    else
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, false>), grid, dim3(kThreads), 0, stream, args);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, hipStream_t stream) {
     PrefillArgs args = a;
     args.n_qtiles = (a.q_len + kBM - 1) / kBM;
-    dim3 grid(args.n_qtiles, a.q_heads, a.batch), block(kThreads);
+    dim3 grid(args.n_qtiles, a.q_heads, a.batch);
     switch (head_dim) {
-        case 32: hipLaunchKernelGGL(prefill_bf16_kernel<32>, grid, block, 0, stream, args); break;
-        case 64: hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, block, 0, stream, args); break;
-        case 128: hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, block, 0, stream, args); break;
+        case 32: return launch_d<32>(args, grid, stream);
+        case 64: return launch_d<64>(args, grid, stream);
+        case 128: return launch_d<128>(args, grid, stream);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace mi_attn
