@@ -46,12 +46,13 @@ constexpr int kBN = 64;     // keys per tile
 constexpr int kThreads = 256;
 constexpr float kRescaleSlack = 8.0f;  // log2 units the stale max may lag behind
 
-// XOR swizzle of the 16-byte chunk index within a row: spreads the 8 rows read by one
-// ds_read_b128 phase and the 4 rows of one transposing read over distinct banks.
-template <int CPR>
-__device__ __forceinline__ int swz(int row) {
-    return ((2 * row + (row >> 2)) & 7) & (CPR - 1);
-}
+// LDS row strides in 16-byte slots.  One ds_read_b128 phase (16 lanes) reads 16
+// consecutive K rows at one chunk: a K row stride of CPR+1 slots puts them in 16
+// distinct slots modulo 256 bytes (gfx950 has 64 four-byte LDS banks).  One
+// ds_read_b64_tr_b16 phase (32 lanes) reads 4 consecutive V rows (aligned to 4) at 64
+// adjacent bytes: a V row stride of CPR+4 slots keeps those 256 bytes distinct modulo 256.
+template <int D> constexpr int k_stride() { return D / 8 + 1; }
+template <int D> constexpr int v_stride() { return D / 8 + 4; }
 
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
@@ -65,44 +66,61 @@ __device__ __forceinline__ float halves_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Copy key tile `kt` of K and V (rows clamped to valid-1: rows past the valid length
-// hold finite copies of a valid row and are masked out of the softmax) into LDS.
-template <int D>
-__device__ __forceinline__ void tile_to_lds(u32x4* k_dst, u32x4* v_dst, const uint16_t* kg, const uint16_t* vg,
-                                            int kt, int valid, int wave, int lane) {
+// One 16-byte-per-lane copy from global memory straight into LDS: lane l's 16 bytes land
+// at lds_base + 16 * l (lds_base must be wave-uniform).  Written as inline assembly so
+// that the compiler does not track it as an outstanding LDS write -- it would otherwise
+// wait for every copy in flight (vmcnt(0)), including the next tile's, before each LDS
+// read -- and the kernel's own vmcnt wait and barrier order the copies against the
+// reads.  Copies the compiler does not see can only make its own vmcnt waits stricter.
+__device__ __forceinline__ void lds_dma16(const void* src, const void* lds_base) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_base;
+    asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0));
+}
+
+// Copy key tile `kt` of K or V into LDS rows of STRIDE slots (16 bytes each).  Lanes that
+// land on a pad slot fetch the row's first chunk again (harmless).  Rows past the valid
+// length are clamped to valid-1: they hold finite copies of a valid row and are masked
+// out of the softmax.
+template <int D, int STRIDE>
+__device__ __forceinline__ void tile_to_lds(u32x4* dst, const uint16_t* src, int kt, int valid, int wave, int lane) {
     constexpr int CPR = D / 8;
-    constexpr int CPT = kBN * CPR / kThreads;
-    typedef __attribute__((address_space(3))) void lds_void;
+    constexpr int NI = kBN * STRIDE / 64;   // wave-wide copy instructions per tile
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-        const int slot0 = (u * (kThreads / 64) + wave) * 64;   // wave-uniform LDS slot base
-        const int p = slot0 + lane;
-        const int row = p / CPR;
-        const int c = (p % CPR) ^ swz<CPR>(row);
-        const int j = min(kt * kBN + row, valid - 1);
-        const size_t off = (size_t)j * D + c * 8;
-        __builtin_amdgcn_global_load_lds((const void*)(kg + off), (lds_void*)(k_dst + slot0), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vg + off), (lds_void*)(v_dst + slot0), 16, 0, 0);
+    for (int i0 = 0; i0 < NI; i0 += kThreads / 64) {
+        const int i = i0 + wave;            // wave-uniform
+        if (i < NI) {
+            const int p = i * 64 + lane;
+            const int row = p / STRIDE;
+            int c = p - row * STRIDE;
+            c = c < CPR ? c : 0;
+            const int j = min(kt * kBN + row, valid - 1);
+            lds_dma16(src + (size_t)j * D + c * 8, dst + i * 64);
+        }
     }
 }
 
 template <int D, bool POS_SCALE>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a) {
-    constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
     constexpr int KC = D / 16;                // MFMA k-steps of Q.K^T
     constexpr int DB = D / 32;                // 32-wide blocks of the output head dim
-    constexpr int TILE = kBN * CPR;           // 16-byte chunks per K (or V) tile
+    constexpr int KS = k_stride<D>();
+    constexpr int VS = v_stride<D>();
 
-    __shared__ __attribute__((aligned(16))) u32x4 lds[2][2][TILE];   // [buffer][K or V][chunk]
+    __shared__ __attribute__((aligned(16))) u32x4 k_lds[2][kBN * KS];
+    __shared__ __attribute__((aligned(16))) u32x4 v_lds[2][kBN * VS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5;                  // half of the wave
-    const int b = blockIdx.z;
-    const int h = blockIdx.y;
-    // causal tiles near the end of the sequence carry the most keys: launch them first
-    const int qt = a.causal ? (a.n_qtiles - 1 - (int)blockIdx.x) : (int)blockIdx.x;
+    // One-dimensional grid, q-tile slowest: for causal attention the tiles near the end of
+    // the sequence carry the most keys, so the whole grid runs longest-first and the short
+    // tiles fill in at the end instead of leaving a tail of long ones.
+    const int bh = (int)(blockIdx.x % (unsigned)(a.batch * a.q_heads));
+    const int qt_rank = (int)(blockIdx.x / (unsigned)(a.batch * a.q_heads));
+    const int b = bh / a.q_heads;
+    const int h = bh % a.q_heads;
+    const int qt = a.causal ? (a.n_qtiles - 1 - qt_rank) : qt_rank;
     const int kvh = h / (a.q_heads / a.kv_heads);
 
     int valid = a.kv_len;
@@ -180,6 +198,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
             qf[kc] = __builtin_bit_cast(bf16x8, w);
         }
     }
+    // Q must have arrived before any copy is in flight: otherwise the compiler's own wait
+    // for Q inside the loop would be a vmcnt(0) that also waits for the next tile's copy
+    __builtin_amdgcn_s_waitcnt(0x0F70);
 
     const size_t kv_head = ((size_t)b * a.kv_heads + kvh) * (size_t)a.kv_len;
     const uint16_t* kg = (const uint16_t*)a.k + kv_head * D;
@@ -193,29 +214,38 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     float l_run = 0.0f;       // running sum over this lane's half of the keys
     const float c2 = a.scale * kLog2e;
 
-    if (kt_begin < kt_end) tile_to_lds<D>(lds[0][0], lds[0][1], kg, vg, kt_begin, valid, wave, lane);
+    if (kt_begin < kt_end) {
+        tile_to_lds<D, KS>(k_lds[0], kg, kt_begin, valid, wave, lane);
+        tile_to_lds<D, VS>(v_lds[0], vg, kt_begin, valid, wave, lane);
+    }
+    typedef __attribute__((address_space(3))) char lds_char;
+    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+    const int k_lane = ((lane & 31) * KS + g) * 16;   // K bytes of (row l%32, chunk g)
+    // bytes of the transposing V read of source lane `lane` (see the P.V step below)
+    const int v_lane = ((4 * g + ((lane & 15) >> 2)) * VS) * 16 + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
     for (int kt = kt_begin; kt < kt_end; ++kt) {
         const int buf = (kt - kt_begin) & 1;
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's copies of tile kt landed
         __syncthreads();                        // ... everyone's; and tile kt-1 is no longer read
-        if (kt + 1 < kt_end) tile_to_lds<D>(lds[buf ^ 1][0], lds[buf ^ 1][1], kg, vg, kt + 1, valid, wave, lane);
+        if (kt + 1 < kt_end) {
+            tile_to_lds<D, KS>(k_lds[buf ^ 1], kg, kt + 1, valid, wave, lane);
+            tile_to_lds<D, VS>(v_lds[buf ^ 1], vg, kt + 1, valid, wave, lane);
+        }
 
         const int kbase = kt * kBN;
         if (!wave_live || kbase > w_union_hi || kbase + kBN - 1 < w_union_lo) continue;
         const bool full = wave_all_rows_valid && kbase >= w_inter_lo && kbase + kBN - 1 <= w_inter_hi;
-        const u32x4* k_t = lds[buf][0];
+        lds_char* const k_t = (lds_char*)(void*)k_lds[buf];
 
         // S^T = K_tile . Q^T : two 32-key blocks
         f32x16 s[2];
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
             s[kb2] = f32x16{};
-            const int row = kb2 * 32 + (lane & 31);
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
-                const int c = 2 * kc + g;
-                const bf16x8 kf = __builtin_bit_cast(bf16x8, k_t[row * CPR + (c ^ swz<CPR>(row))]);
+                const bf16x8 kf = __builtin_bit_cast(bf16x8, *(lds_u32x4*)(k_t + k_lane + (kb2 * 32 * KS + 2 * kc) * 16));
                 s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kc], s[kb2], 0, 0, 0);
             }
         }
@@ -282,19 +312,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
 
         // O^T += V^T . P^T; V^T via transposing reads. Within 16-lane group G = lane/16,
         // source lane s points at key 16*c4 + 4*g + s/4 (+8), dims 32*db + 16*(G%2) + 4*(s%4).
-        const int sl = lane & 15;
-        const int dhalf = (lane >> 4) & 1;
-        void* v_t = (void*)lds[buf][1];
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        lds_char* const v_t = (lds_char*)(void*)v_lds[buf] + v_lane;
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
-            const int r0 = 16 * c4 + 4 * g + (sl >> 2);
-            const int r1 = r0 + 8;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const int col = 32 * db + 16 * dhalf + 4 * (sl & 3);
-                const int ch = col >> 3, sub = (col & 7) * 2;
-                const s16x4 lo = lds_read_tr16(v_t, (r0 * CPR + (ch ^ swz<CPR>(r0))) * 16 + sub);
-                const s16x4 hi = lds_read_tr16(v_t, (r1 * CPR + (ch ^ swz<CPR>(r1))) * 16 + sub);
+                const int imm = (16 * c4 * VS) * 16 + 64 * db;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v_t + imm));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v_t + imm + 8 * VS * 16));
                 typedef __attribute__((ext_vector_type(8))) short s16x8;
                 const s16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[c4], o[db],
@@ -335,7 +361,7 @@ hipError_t launch_d(const PrefillArgs& args, dim3 grid, hipStream_t stream) {
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, hipStream_t stream) {
     PrefillArgs args = a;
     args.n_qtiles = (a.q_len + kBM - 1) / kBM;
-    dim3 grid(args.n_qtiles, a.q_heads, a.batch);
+    dim3 grid((unsigned)args.n_qtiles * a.q_heads * a.batch);
     switch (head_dim) {
         case 32: return launch_d<32>(args, grid, stream);
         case 64: return launch_d<64>(args, grid, stream);
