@@ -12,11 +12,12 @@
 // key tiles.
 //
 // Work decomposition: one workgroup = 4 waves = 128 query rows of one (item, head);
-// wave w owns rows [32w, 32w+32).  Key tiles of 64 rows of K and V are copied from HBM
-// straight into LDS (global_load_lds_dwordx4, 16 bytes per lane, no registers), double
-// buffered so that the copy of tile t+1 overlaps the math on tile t, with one barrier
-// per tile.  16-byte chunks are XOR-swizzled per row (the swizzle is applied on the
-// global side: each lane fetches the chunk that belongs at its LDS slot).
+// wave w owns rows [32w, 32w+32).  The grid is one-dimensional with the q-tile index
+// slowest (longest causal tiles first).  Key tiles of 64 rows of K and V are copied from
+// HBM straight into LDS (global_load_lds_dwordx4, 16 bytes per lane, no registers),
+// double buffered so that the copy of tile t+1 overlaps the math on tile t, with one
+// barrier per tile.  LDS rows are padded (K: D/8+1, V: D/8+4 sixteen-byte slots) so
+// that both the 128-bit K reads and the transposing V reads are free of bank conflicts.
 //
 // Per wave and key tile:
 //   S^T (64 keys x 32 rows) = K_tile (A operand, from LDS) x Q^T (B operand, registers).
