@@ -12,6 +12,9 @@ same line, each with a roofline object.  Kernel times come from HIP events recor
 the stream the kernels run on.  `--workload` benchmarks one other named workload alone.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+`--workload copy_calibration` runs a plain 1 GiB device copy instead, the known-size
+reference against which the rocprofv3 FETCH_SIZE / WRITE_SIZE counters are scaled.
 """
 from __future__ import annotations
 
@@ -198,6 +201,36 @@ def cpu_baseline_decode(w: W.Workload, x: dict, budget_s: float) -> dict:
 
 
 # ---------------------------------------------------------------------------
+# HBM counter calibration: a plain device-to-device copy of a known size
+
+
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration(steps: int, warmup: int) -> int:
+    """Copies 1 GiB between two device buffers `steps` times.  Under rocprofv3 --pmc the
+    FETCH_SIZE / WRITE_SIZE this copy reports, against its known 1 GiB read and 1 GiB
+    written, gives the factor that turns those counters into bytes for the attention
+    kernels measured the same way."""
+    import torch
+    src = torch.full((COPY_BYTES,), 7, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    begin, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    begin.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    end.record()
+    torch.cuda.synchronize()
+    ms = begin.elapsed_time(end) / max(steps, 1)
+    print(json.dumps({"workload": "copy_calibration", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                      "ms_per_copy": ms, "GBps": 2 * COPY_BYTES / (ms / 1e3) / 1e9}), flush=True)
+    return 0
+
+
+# ---------------------------------------------------------------------------
 
 
 def main() -> int:
@@ -206,7 +239,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="headline",
-                    help="headline (prefill causal_gqa_s4096 + decode gqa_decode_kv8192) or a name in workloads.WORKLOADS")
+                    help="headline (prefill causal_gqa_s4096 + decode gqa_decode_kv8192), a name in "
+                         "workloads.WORKLOADS, or copy_calibration (1 GiB device copy for the HBM counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work per baseline")
     args = ap.parse_args()
@@ -222,6 +256,8 @@ def main() -> int:
     import head_attention_02_amd as mi
     mi.library()
 
+    if args.workload == "copy_calibration":
+        return copy_calibration(args.steps, args.warmup)
     if args.workload == "headline":
         names = ["causal_gqa_s4096", "gqa_decode_kv8192"]
     else:
