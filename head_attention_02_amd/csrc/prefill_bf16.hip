@@ -14,10 +14,8 @@
 // Work decomposition: one workgroup = 4 waves = 128 query rows of one (item, head);
 // wave w owns rows [32w, 32w+32).  The grid is one-dimensional with the q-tile index
 // slowest (longest causal tiles first).  Key tiles of 64 rows of K and V are copied from
-// HBM straight into LDS (global_load_lds_dwordx4, 16 bytes per lane, no registers),
-// double buffered so that the copy of tile t+1 overlaps the math on tile t, with one
-// barrier per tile.  LDS rows are padded (K: D/8+1, V: D/8+4 sixteen-byte slots) so
-// that both the 128-bit K reads and the transposing V reads are free of bank conflicts.
+// HBM straight into LDS (global_load_lds_dwordx4, 16 bytes per lane, no registers) with
+// per-lane offsets computed once; one barrier per tile.
 //
 // Per wave and key tile:
 //   S^T (64 keys x 32 rows) = K_tile (A operand, from LDS) x Q^T (B operand, registers).
@@ -31,11 +29,24 @@
 //   operands (P from the accumulator layout, V by the LDS addresses), which leaves the
 //   contraction unchanged.
 //
+// Software pipeline: the loop body for tile t issues the Q.K^T MFMAs of tile t+1 next
+// to the exp/pack work of tile t (matrix core and vector ALU run side by side), then
+// the P.V MFMAs of tile t next to the row max of tile t+1.  K is therefore kept one
+// tile ahead of V: the copies issued in the body of tile t are K(t+2) and V(t+1), each
+// into the buffer its predecessor vacated.
+//
 // Softmax bookkeeping per tile, for scale > 0: the max is taken over raw scores and the
 // scale is folded into one FMA per score, p = exp2(s*c - m*c) with c = scale*log2(e).
 // The running max is only moved (and O, l rescaled) when the tile's max exceeds it by
 // more than 2^8; otherwise the stale max is kept, p <= 256, and the final O / l is
 // unchanged because numerator and denominator share it.
+//
+// LDS layout (bank conflicts): gfx950 LDS has 64 four-byte banks.  One ds_read_b128
+// phase (16 lanes) reads 16 consecutive K rows at one 16-byte chunk, so K rows are
+// padded to D/8+1 chunks.  One ds_read_b64_tr_b16 phase (32 lanes) reads 4 consecutive V
+// rows at one 64-byte column group, so V rows are XOR-swizzled at 64-byte granularity:
+// chunk c of row r sits at chunk c ^ vswz(r), which puts the four rows in four
+// different quarters of the 256 bytes the banks cover.
 #include "mi_attn_device.hpp"
 #include "mi_attn_kernels.hpp"
 
@@ -47,17 +58,36 @@ constexpr int kBN = 64;     // keys per tile
 constexpr int kThreads = 256;
 constexpr float kRescaleSlack = 8.0f;  // log2 units the stale max may lag behind
 
-// LDS row strides in 16-byte slots.  One ds_read_b128 phase (16 lanes) reads 16
-// consecutive K rows at one chunk: a K row stride of CPR+1 slots puts them in 16
-// distinct slots modulo 256 bytes (gfx950 has 64 four-byte LDS banks).  One
-// ds_read_b64_tr_b16 phase (32 lanes) reads 4 consecutive V rows (aligned to 4) at 64
-// adjacent bytes: a V row stride of CPR+4 slots keeps those 256 bytes distinct modulo 256.
-template <int D> constexpr int k_stride() { return D / 8 + 1; }
-template <int D> constexpr int v_stride() { return D / 8 + 4; }
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <int D>
+struct Geo {
+    static constexpr int CPR = D / 8;            // 16-byte chunks per row
+    static constexpr int KC = D / 16;            // MFMA k-steps of Q.K^T
+    static constexpr int DB = D / 32;            // 32-wide blocks of the output head dim
+    static constexpr int KS = CPR + 1;           // K row stride in chunks (padded)
+    static constexpr int NK = kBN * KS / 64;     // K copy instructions per tile
+    static constexpr int NKW = (NK + 3) / 4;     // ... per wave (at most)
+    static constexpr int NV = kBN * CPR / 64;    // V copy instructions per tile
+    static constexpr int NVW = NV / 4;           // ... per wave
+    static constexpr int K_BYTES = kBN * KS * 16;
+    static constexpr int V_BYTES = kBN * CPR * 16;
+    static_assert(NV % 4 == 0, "V copies split evenly over the waves");
+};
+
+// V swizzle: XOR applied to the chunk index of row r (multiples of 4 chunks = 64 bytes).
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+    constexpr int QR = D / 32;        // 64-byte quarters per row
+    constexpr int RP = 4 / QR;        // rows per 256 bytes
+    return 4 * ((r / RP) & (QR - 1));
+}
 
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
-// Row max over both halves of the wave (lanes l and l^32 hold the same query row).
+// Row max / sum over both halves of the wave (lanes l and l^32 hold the same query row).
 __device__ __forceinline__ float halves_max(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -67,53 +97,202 @@ __device__ __forceinline__ float halves_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// One 16-byte-per-lane copy from global memory straight into LDS: lane l's 16 bytes land
-// at lds_base + 16 * l (lds_base must be wave-uniform).  Written as inline assembly so
-// that the compiler does not track it as an outstanding LDS write -- it would otherwise
-// wait for every copy in flight (vmcnt(0)), including the next tile's, before each LDS
-// read -- and the kernel's own vmcnt wait and barrier order the copies against the
-// reads.  Copies the compiler does not see can only make its own vmcnt waits stricter.
-__device__ __forceinline__ void lds_dma16(const void* src, const void* lds_base) {
-    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_base;
-    asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0));
+
+// One 16-byte-per-lane copy from global memory straight into LDS: lane l reads
+// sbase + voff and its 16 bytes land at LDS address m0 + 16 * l (sbase and m0 are
+// wave-uniform).  Written as inline assembly so that the compiler does not track it as
+// an outstanding LDS write -- it would otherwise wait for every copy in flight
+// (vmcnt(0)), including the next tile's, before each LDS read -- and the kernel's own
+// vmcnt wait and barrier order the copies against the reads.
+__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t m0) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(m0));
 }
 
-// Copy key tile `kt` of K or V into LDS rows of STRIDE slots (16 bytes each).  Lanes that
-// land on a pad slot fetch the row's first chunk again (harmless).  Rows past the valid
-// length are clamped to valid-1: they hold finite copies of a valid row and are masked
-// out of the softmax.
-template <int D, int STRIDE>
-__device__ __forceinline__ void tile_to_lds(u32x4* dst, const uint16_t* src, int kt, int valid, int wave, int lane) {
-    constexpr int CPR = D / 8;
-    constexpr int NI = kBN * STRIDE / 64;   // wave-wide copy instructions per tile
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Marks a rarely taken, wave-uniform branch as having a side effect so that the compiler
+// keeps it a branch instead of computing its body on every tile and selecting.
+__device__ __forceinline__ void keep_branch() { asm volatile("" ::); }
+
+template <int D, bool POS_SCALE>
+struct Prefill {
+    using G = Geo<D>;
+
+    // ---- per-lane constants ---------------------------------------------------------
+    int lane, wave, g;
+    int kvalid;                 // valid key rows of this item
+    const char* kg;             // K rows of this (item, kv head)
+    const char* vg;
+    uint32_t k_lds0, v_lds0;    // LDS byte addresses of buffer 0
+    uint32_t koff[G::NKW];      // byte offsets of this lane's K copy chunks inside a tile
+    uint32_t voff;              // ... V (first copy; the others are +4096 bytes each)
+    int k_read;                 // LDS byte offset of this lane's K operand (row l%32, chunk g)
+    int v_read[G::DB];          // LDS byte offsets of this lane's transposing V reads
+    int lo_r, hi_r;             // this lane's key interval
+    bool wave_all_rows_valid;
+    int w_inter_lo, w_inter_hi; // keys every row of the wave sees
+    float c2;                   // scale * log2(e)
+
+    // ---- running state ----------------------------------------------------------------
+    bf16x8 qf[G::KC];
+    f32x16 o[G::DB];
+    float m_run, l_run;
+
+    __device__ __forceinline__ void copy_k(int kt, int par) {
+        const char* base = kg + (size_t)kt * kBN * D * 2;
+        const bool tail = kt * kBN + kBN > kvalid;
 #pragma unroll
-    for (int i0 = 0; i0 < NI; i0 += kThreads / 64) {
-        const int i = i0 + wave;            // wave-uniform
-        if (i < NI) {
-            const int p = i * 64 + lane;
-            const int row = p / STRIDE;
-            int c = p - row * STRIDE;
-            c = c < CPR ? c : 0;
-            const int j = min(kt * kBN + row, valid - 1);
-            lds_dma16(src + (size_t)j * D + c * 8, dst + i * 64);
+        for (int ii = 0; ii < G::NKW; ++ii) {
+            const int i = wave + 4 * ii;
+            if (i < G::NK) {
+                uint32_t off = koff[ii];
+                if (tail) {   // rows past the valid length repeat the last valid row
+                    const int p = i * 64 + lane;
+                    int row = p / G::KS, c = p - (p / G::KS) * G::KS;
+                    c = c < G::CPR ? c : 0;
+                    row = min(row, kvalid - 1 - kt * kBN);
+                    off = (uint32_t)((row * D + c * 8) * 2);
+                }
+                lds_dma16(base, off, k_lds0 + par * G::K_BYTES + i * 1024);
+            }
         }
     }
-}
+
+    __device__ __forceinline__ void copy_v(int kt, int par) {
+        const char* base = vg + (size_t)kt * kBN * D * 2;
+        const bool tail = kt * kBN + kBN > kvalid;
+#pragma unroll
+        for (int ii = 0; ii < G::NVW; ++ii) {
+            const int i = wave + 4 * ii;
+            uint32_t off = voff;
+            const char* b = base + ii * 4096;
+            if (tail) {
+                const int p = i * 64 + lane;
+                int row = p / G::CPR;
+                const int c = (p % G::CPR) ^ vswz<D>(row);
+                row = min(row, kvalid - 1 - kt * kBN);
+                off = (uint32_t)((row * D + c * 8) * 2);
+                b = base;
+            }
+            lds_dma16(b, off, v_lds0 + par * G::V_BYTES + i * 1024);
+        }
+    }
+
+    // S^T = K_tile . Q^T : two 32-key blocks
+    __device__ __forceinline__ void qk(f32x16 (&s)[2], const lds_char* kbuf) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            s[kb2] = f32x16{};
+#pragma unroll
+            for (int kc = 0; kc < G::KC; ++kc) {
+                const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(kbuf + k_read + (kb2 * 32 * G::KS + 2 * kc) * 16));
+                s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kc], s[kb2], 0, 0, 0);
+            }
+        }
+    }
+
+    // Masks the scores of tile kt for rows that do not see every key of it (and scales
+    // them when the scale is not positive); element e of block kb2 is key
+    // kt*64 + 32*kb2 + 8*(e/4) + 4*g + e%4.
+    __device__ __forceinline__ void mask_scale(f32x16 (&s)[2], int kt) {
+        const int kbase = kt * kBN;
+        const bool full = wave_all_rows_valid && kbase >= w_inter_lo && kbase + kBN - 1 <= w_inter_hi;
+        if (!full) {
+            keep_branch();
+            const int lo = lo_r - kbase - 4 * g, hi = hi_r - kbase - 4 * g;
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int jj = 32 * kb2 + 8 * (e / 4) + (e % 4);
+                    if (!POS_SCALE) s[kb2][e] *= c2;
+                    s[kb2][e] = (jj >= lo && jj <= hi) ? s[kb2][e] : kNegInf;
+                }
+        } else if (!POS_SCALE) {
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] *= c2;
+        }
+    }
+
+    // Row max of a (masked) score tile in log2 units, then the lazy rescale.
+    __device__ __forceinline__ void update_max(const f32x16 (&s)[2]) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) mx = max3(mx, s[kb2][e], s[kb2][e + 1]);
+        mx = halves_max(mx);
+        const float m_tile = POS_SCALE ? mx * c2 : mx;
+        const bool need = m_tile > m_run + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            keep_branch();
+            const float alpha = need ? fast_exp2(m_run - m_tile) : 1.0f;
+            m_run = need ? m_tile : m_run;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < G::DB; ++i) o[i] *= alpha;
+        }
+    }
+
+    // Probabilities of a score tile -> packed bf16 P^T operands; P chunk c4 (16 keys) =
+    // block c4/2, elements 8*(c4%2) + [0, 8).  Adds the row sum of the fp32 values.
+    __device__ __forceinline__ void probs(const f32x16 (&s)[2], bf16x8 (&pf)[4]) {
+        const float m_use = m_run == kNegInf ? 0.0f : m_run;
+        float ls0 = 0.0f, ls1 = 0.0f;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            u32x4 w;
+#pragma unroll
+            for (int jj = 0; jj < 8; jj += 2) {
+                const float s0 = s[c4 / 2][8 * (c4 % 2) + jj], s1 = s[c4 / 2][8 * (c4 % 2) + jj + 1];
+                const float p0 = POS_SCALE ? fast_exp2(fmaf(s0, c2, -m_use)) : fast_exp2(s0 - m_use);
+                const float p1 = POS_SCALE ? fast_exp2(fmaf(s1, c2, -m_use)) : fast_exp2(s1 - m_use);
+                w[jj / 2] = pack_bf16x2(p0, p1);
+                ls0 += p0;
+                ls1 += p1;
+            }
+            pf[c4] = __builtin_bit_cast(bf16x8, w);
+        }
+        l_run += ls0 + ls1;
+    }
+
+    // O^T += V^T . P^T; V^T via transposing reads.  Within 16-lane group G = lane/16,
+    // source lane s points at key 16*c4 + 4*g + s/4 (+8), dims 32*db + 16*(G%2) + 4*(s%4).
+    __device__ __forceinline__ void pv(const bf16x8 (&pf)[4], const lds_char* vbuf) {
+        constexpr int RB = 2 * D;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db) {
+                const lds_char* p = vbuf + v_read[db] + 16 * c4 * RB;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * RB));
+                typedef __attribute__((ext_vector_type(8))) short s16x8;
+                const s16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[c4], o[db], 0, 0, 0);
+            }
+        }
+    }
+};
 
 template <int D, bool POS_SCALE>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a) {
-    constexpr int KC = D / 16;                // MFMA k-steps of Q.K^T
-    constexpr int DB = D / 32;                // 32-wide blocks of the output head dim
-    constexpr int KS = k_stride<D>();
-    constexpr int VS = v_stride<D>();
+    using G = Geo<D>;
+    __shared__ __attribute__((aligned(16))) u32x4 k_lds[2][kBN * G::KS];
+    __shared__ __attribute__((aligned(16))) u32x4 v_lds[2][kBN * G::CPR];
 
-    __shared__ __attribute__((aligned(16))) u32x4 k_lds[2][kBN * KS];
-    __shared__ __attribute__((aligned(16))) u32x4 v_lds[2][kBN * VS];
-
+    Prefill<D, POS_SCALE> st;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5;                  // half of the wave
+    st.lane = lane;
+    st.wave = wave;
+    st.g = g;
     // One-dimensional grid, q-tile slowest: for causal attention the tiles near the end of
     // the sequence carry the most keys, so the whole grid runs longest-first and the short
     // tiles fill in at the end instead of leaving a tail of long ones.
@@ -126,6 +305,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
 
     int valid = a.kv_len;
     if (a.seq_lens) valid = min(max(a.seq_lens[b], 0), a.kv_len);
+    st.kvalid = valid;
 
     const int q0 = qt * kBM;
     const int last_row = min(q0 + kBM, a.q_len) - 1;
@@ -163,186 +343,138 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
         }
     }
     if (my_pos >= valid || my_row >= a.q_len) hi_r = -1;
+    st.lo_r = lo_r;
+    st.hi_r = hi_r;
 
-    // the same for the wave as a whole (uniform): union and intersection of row intervals
+    // keys that every row of the wave sees (uniform)
     const int w_row0 = q0 + wave * 32;
     const int w_row1 = min(w_row0 + 31, a.q_len - 1);
-    const bool wave_live = w_row0 < a.q_len && a.pos_offset + w_row0 < valid;
     const int wp_lo = a.pos_offset + w_row0, wp_hi = a.pos_offset + w_row1;
-    int w_union_lo = 0, w_union_hi = valid - 1, w_inter_lo = 0, w_inter_hi = valid - 1;
-    if (a.causal) {
-        w_union_hi = min(w_union_hi, wp_hi);
-        w_inter_hi = min(w_inter_hi, wp_lo);
-    }
+    int w_inter_lo = 0, w_inter_hi = valid - 1;
+    if (a.causal) w_inter_hi = min(w_inter_hi, wp_lo);
     if (a.window > 0) {
         if (a.causal) {
-            w_union_lo = max(0, wp_lo - a.window + 1);
             w_inter_lo = max(0, wp_hi - a.window + 1);
         } else {
-            w_union_lo = max(0, wp_lo - half_w);
             w_inter_lo = max(0, wp_hi - half_w);
-            w_union_hi = min(w_union_hi, wp_hi + half_w);
             w_inter_hi = min(w_inter_hi, wp_lo + half_w);
         }
     }
-    const bool wave_all_rows_valid = wp_hi < valid;
+    st.w_inter_lo = w_inter_lo;
+    st.w_inter_hi = w_inter_hi;
+    st.wave_all_rows_valid = w_row0 < a.q_len && wp_hi < valid;
 
     // ---- Q^T operand: lane l holds row l%32, dims 16*kc + 8*g + [0, 8) ---------------
     const size_t q_head = ((size_t)b * a.q_heads + h) * (size_t)a.q_len;
-    bf16x8 qf[KC];
     {
         const uint16_t* qrow = (const uint16_t*)a.q + (q_head + (size_t)min(my_row, a.q_len - 1)) * D;
         const bool in = my_row < a.q_len;
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
+        for (int kc = 0; kc < G::KC; ++kc) {
             u32x4 w = in ? *(const u32x4*)(qrow + 16 * kc + 8 * g) : u32x4{0, 0, 0, 0};
-            qf[kc] = __builtin_bit_cast(bf16x8, w);
+            st.qf[kc] = __builtin_bit_cast(bf16x8, w);
         }
     }
     // Q must have arrived before any copy is in flight: otherwise the compiler's own wait
     // for Q inside the loop would be a vmcnt(0) that also waits for the next tile's copy
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    wait_vm0();
 
     const size_t kv_head = ((size_t)b * a.kv_heads + kvh) * (size_t)a.kv_len;
-    const uint16_t* kg = (const uint16_t*)a.k + kv_head * D;
-    const uint16_t* vg = (const uint16_t*)a.v + kv_head * D;
-
-    // ---- running state ----------------------------------------------------------------
-    f32x16 o[DB];
+    st.kg = (const char*)((const uint16_t*)a.k + kv_head * D);
+    st.vg = (const char*)((const uint16_t*)a.v + kv_head * D);
+    st.k_lds0 = lds_addr(k_lds[0]);
+    st.v_lds0 = lds_addr(v_lds[0]);
 #pragma unroll
-    for (int i = 0; i < DB; ++i) o[i] = f32x16{};
-    float m_run = kNegInf;    // running (possibly stale) max of this lane's row, log2 units
-    float l_run = 0.0f;       // running sum over this lane's half of the keys
-    const float c2 = a.scale * kLog2e;
-
-    if (kt_begin < kt_end) {
-        tile_to_lds<D, KS>(k_lds[0], kg, kt_begin, valid, wave, lane);
-        tile_to_lds<D, VS>(v_lds[0], vg, kt_begin, valid, wave, lane);
+    for (int ii = 0; ii < G::NKW; ++ii) {
+        const int p = (wave + 4 * ii) * 64 + lane;
+        const int row = p / G::KS;
+        int c = p - row * G::KS;
+        c = c < G::CPR ? c : 0;
+        st.koff[ii] = (uint32_t)((row * D + c * 8) * 2);
     }
-    typedef __attribute__((address_space(3))) char lds_char;
-    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-    const int k_lane = ((lane & 31) * KS + g) * 16;   // K bytes of (row l%32, chunk g)
-    // bytes of the transposing V read of source lane `lane` (see the P.V step below)
-    const int v_lane = ((4 * g + ((lane & 15) >> 2)) * VS) * 16 + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-        const int buf = (kt - kt_begin) & 1;
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's copies of tile kt landed
-        __syncthreads();                        // ... everyone's; and tile kt-1 is no longer read
-        if (kt + 1 < kt_end) {
-            tile_to_lds<D, KS>(k_lds[buf ^ 1], kg, kt + 1, valid, wave, lane);
-            tile_to_lds<D, VS>(v_lds[buf ^ 1], vg, kt + 1, valid, wave, lane);
+    {
+        const int p = wave * 64 + lane;
+        const int row = p / G::CPR;
+        const int c = (p % G::CPR) ^ vswz<D>(row);
+        st.voff = (uint32_t)((row * D + c * 8) * 2);
+    }
+    st.k_read = ((lane & 31) * G::KS + g) * 16;
+    {
+        const int r = 4 * g + ((lane & 15) >> 2);
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db) {
+            const int cb = 64 * db + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);   // column byte
+            st.v_read[db] = r * 2 * D + 16 * ((cb >> 4) ^ vswz<D>(r)) + (cb & 15);
         }
+    }
+    st.c2 = a.scale * kLog2e;
+#pragma unroll
+    for (int i = 0; i < G::DB; ++i) st.o[i] = f32x16{};
+    st.m_run = kNegInf;    // running (possibly stale) max of this lane's row, log2 units
+    st.l_run = 0.0f;       // running sum over this lane's half of the keys
 
-        const int kbase = kt * kBN;
-        if (!wave_live || kbase > w_union_hi || kbase + kBN - 1 < w_union_lo) continue;
-        const bool full = wave_all_rows_valid && kbase >= w_inter_lo && kbase + kBN - 1 <= w_inter_hi;
-        lds_char* const k_t = (lds_char*)(void*)k_lds[buf];
+    const lds_char* kb[2] = {(const lds_char*)(const void*)k_lds[0], (const lds_char*)(const void*)k_lds[1]};
+    const lds_char* vb[2] = {(const lds_char*)(const void*)v_lds[0], (const lds_char*)(const void*)v_lds[1]};
 
-        // S^T = K_tile . Q^T : two 32-key blocks
-        f32x16 s[2];
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-            s[kb2] = f32x16{};
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                const bf16x8 kf = __builtin_bit_cast(bf16x8, *(lds_u32x4*)(k_t + k_lane + (kb2 * 32 * KS + 2 * kc) * 16));
-                s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kc], s[kb2], 0, 0, 0);
-            }
-        }
-
-        // mask: element e of block kb2 is key kbase + 32*kb2 + 8*(e/4) + 4*g + e%4
-        if (!full) {
-            const int lo = lo_r - kbase - 4 * g, hi = hi_r - kbase - 4 * g;
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int jj = 32 * kb2 + 8 * (e / 4) + (e % 4);
-                    if (!POS_SCALE) s[kb2][e] *= c2;
-                    s[kb2][e] = (jj >= lo && jj <= hi) ? s[kb2][e] : kNegInf;
-                }
-        } else if (!POS_SCALE) {
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] *= c2;
-        }
-
-        // tile row max (raw scores when scale > 0, scaled scores otherwise)
-        float mx = kNegInf;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int e = 0; e < 16; e += 2) mx = max3(mx, s[kb2][e], s[kb2][e + 1]);
-        mx = halves_max(mx);
-        const float m_tile = POS_SCALE ? mx * c2 : mx;
-
-        // lazy rescale: move the running max only when the tile's max runs ahead of it
-        const bool need = m_tile > m_run + kRescaleSlack;
-        if (__builtin_amdgcn_ballot_w64(need)) {
-            const float alpha = need ? fast_exp2(m_run - m_tile) : 1.0f;
-            m_run = need ? m_tile : m_run;
-            l_run *= alpha;
-#pragma unroll
-            for (int i = 0; i < DB; ++i) o[i] *= alpha;
-        }
-        const float m_use = m_run == kNegInf ? 0.0f : m_run;
-
-        // probabilities -> packed bf16 B operands; P chunk c4 (16 keys) = block c4/2,
-        // elements 8*(c4%2) + [0, 8).
+    // One pipelined step for tile kt = kt_begin + j (buffer parity PAR = j & 1): cur holds
+    // the masked scores of tile kt with the running max already updated for it.
+    auto step = [&](auto has_next_c, auto par_c, f32x16 (&cur)[2], f32x16 (&nxt)[2], int j) {
+        constexpr bool HAS_NEXT = decltype(has_next_c)::value;
+        constexpr int PAR = decltype(par_c)::value;
+        const int kt = kt_begin + j;
+        wait_vm0();          // this thread's copies of K(kt+1) and V(kt) have landed
+        __syncthreads();     // ... everyone's; and nobody still reads K(kt) or V(kt-1)
+        if (kt + 2 < kt_end) st.copy_k(kt + 2, PAR);
+        if (HAS_NEXT) st.copy_v(kt + 1, PAR ^ 1);
         bf16x8 pf[4];
-        float lsum0 = 0.0f, lsum1 = 0.0f;
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-            u32x4 w;
-#pragma unroll
-            for (int jj = 0; jj < 8; jj += 2) {
-                float p0, p1;
-                if (POS_SCALE) {
-                    p0 = fast_exp2(fmaf(s[c4 / 2][8 * (c4 % 2) + jj], c2, -m_use));
-                    p1 = fast_exp2(fmaf(s[c4 / 2][8 * (c4 % 2) + jj + 1], c2, -m_use));
-                } else {
-                    p0 = fast_exp2(s[c4 / 2][8 * (c4 % 2) + jj] - m_use);
-                    p1 = fast_exp2(s[c4 / 2][8 * (c4 % 2) + jj + 1] - m_use);
-                }
-                w[jj / 2] = pack_bf16x2(p0, p1);
-                lsum0 += p0; lsum1 += p1;
-            }
-            pf[c4] = __builtin_bit_cast(bf16x8, w);
-        }
-        l_run += lsum0 + lsum1;
+        if (HAS_NEXT) st.qk(nxt, kb[PAR ^ 1]);
+        st.probs(cur, pf);
+        if (HAS_NEXT) st.mask_scale(nxt, kt + 1);
+        st.pv(pf, vb[PAR]);
+        if (HAS_NEXT) st.update_max(nxt);
+    };
 
-        // O^T += V^T . P^T; V^T via transposing reads. Within 16-lane group G = lane/16,
-        // source lane s points at key 16*c4 + 4*g + s/4 (+8), dims 32*db + 16*(G%2) + 4*(s%4).
-        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-        lds_char* const v_t = (lds_char*)(void*)v_lds[buf] + v_lane;
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int imm = (16 * c4 * VS) * 16 + 64 * db;
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v_t + imm));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v_t + imm + 8 * VS * 16));
-                typedef __attribute__((ext_vector_type(8))) short s16x8;
-                const s16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[c4], o[db],
-                                                               0, 0, 0);
-            }
+    const int n = kt_end - kt_begin;
+    if (n > 0) {
+        f32x16 sa[2], sb[2];
+        st.copy_k(kt_begin, 0);
+        wait_vm0();
+        __syncthreads();
+        if (n > 1) st.copy_k(kt_begin + 1, 1);
+        st.copy_v(kt_begin, 0);
+        st.qk(sa, kb[0]);
+        st.mask_scale(sa, kt_begin);
+        st.update_max(sa);
+        typedef std::integral_constant<bool, true> T_;
+        typedef std::integral_constant<bool, false> F_;
+        typedef std::integral_constant<int, 0> P0;
+        typedef std::integral_constant<int, 1> P1;
+        int j = 0;
+        for (; j + 2 < n; j += 2) {
+            step(T_{}, P0{}, sa, sb, j);
+            step(T_{}, P1{}, sb, sa, j + 1);
+        }
+        if (j + 1 < n) {
+            step(T_{}, P0{}, sa, sb, j);
+            step(F_{}, P1{}, sb, sa, j + 1);
+        } else {
+            step(F_{}, P0{}, sa, sb, j);
         }
     }
 
     // ---- epilogue: normalise, zero padded / empty rows, store bf16 --------------------
-    const float l_tot = halves_sum(l_run);
+    const float l_tot = halves_sum(st.l_run);
     if (my_row >= a.q_len) return;
     const float inv = (hi_r >= 0 && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
     uint16_t* orow = (uint16_t*)a.out + (q_head + (size_t)my_row) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < G::DB; ++db) {
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
             const int d = 32 * db + 8 * e4 + 4 * g;
             u32x2 w;
-            w[0] = pack_bf16x2(o[db][4 * e4] * inv, o[db][4 * e4 + 1] * inv);
-            w[1] = pack_bf16x2(o[db][4 * e4 + 2] * inv, o[db][4 * e4 + 3] * inv);
+            w[0] = pack_bf16x2(st.o[db][4 * e4] * inv, st.o[db][4 * e4 + 1] * inv);
+            w[1] = pack_bf16x2(st.o[db][4 * e4 + 2] * inv, st.o[db][4 * e4 + 3] * inv);
             *(u32x2*)(orow + d) = w;
         }
     }
