@@ -304,7 +304,12 @@ def main() -> int:
         if w.kind == "prefill":
             fl = prefill_flops(w, x["seq_lens"])
             peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-            src = ["prefill_bf16.hip" if w.dtype == "bf16" else "prefill_f32.hip", "mi_attn_device.hpp"]
+            if w.dtype != "bf16":
+                src = ["prefill_f32.hip", "mi_attn_device.hpp"]
+            elif w.head_dim == 128:
+                src = ["prefill_bf16.hip", "mi_attn_device.hpp"]
+            else:
+                src = ["prefill_bf16_narrow.hip", "mi_attn_device.hpp"]
             rooflines[w.name] = {"bound": "mfma", "achieved": fl / sec / 1e12, "peak": peak, "unit": "TFLOP/s",
                                  "frac": fl / sec / 1e12 / peak,
                                  "traffic": traffic_from_profiles(w.name, kernel_sources_digest(src)),

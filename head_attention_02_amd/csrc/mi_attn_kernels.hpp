@@ -37,6 +37,8 @@ struct DecodeArgs {
 
 // Each launcher enqueues on `stream` and returns the launch status.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, hipStream_t stream);
+// head dims 32 and 64 (called by launch_prefill_bf16)
+hipError_t launch_prefill_bf16_narrow(const PrefillArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int heads_per_group, bool bf16,
                          hipStream_t stream);

@@ -1,4 +1,5 @@
-// prefill_bf16.hip -- fused attention prefill for bf16 inputs on gfx950 matrix cores.
+// prefill_bf16.hip -- fused attention prefill for bf16 inputs on gfx950 matrix cores
+// (head dim 128; head dims 32 and 64 run prefill_bf16_narrow.hip).
 //
 // Computes softmax(scale * Q K^T + mask) V per (item, query head) in one pass over the
 // keys, without materialising the score matrix: the scores of one key tile live in
@@ -11,11 +12,11 @@
 // the band (ripvec-core `Driver`, `banded_qk`), which here is done by skipping whole
 // key tiles.
 //
-// Work decomposition: one workgroup = 4 waves = 128 query rows of one (item, head);
+// Work decomposition: one workgroup = 8 waves = 256 query rows of one (item, head);
 // wave w owns rows [32w, 32w+32).  The grid is one-dimensional with the q-tile index
-// slowest (longest causal tiles first).  Key tiles of 64 rows of K and V are copied from
-// HBM straight into LDS (global_load_lds_dwordx4, 16 bytes per lane, no registers) with
-// per-lane offsets computed once; one barrier per tile.
+// slowest (longest causal tiles first) and XCD-aware.  Key tiles of 64 rows of K and V
+// are copied from HBM straight into LDS (global_load_lds_dwordx4, 16 bytes per lane, no
+// registers, per-lane offsets computed once), double buffered.
 //
 // Per wave and key tile:
 //   S^T (64 keys x 32 rows) = K_tile (A operand, from LDS) x Q^T (B operand, registers).
@@ -29,11 +30,11 @@
 //   operands (P from the accumulator layout, V by the LDS addresses), which leaves the
 //   contraction unchanged.
 //
-// Software pipeline: the loop body for tile t issues the Q.K^T MFMAs of tile t+1 next
-// to the exp/pack work of tile t (matrix core and vector ALU run side by side), then
-// the P.V MFMAs of tile t next to the row max of tile t+1.  K is therefore kept one
-// tile ahead of V: the copies issued in the body of tile t are K(t+2) and V(t+1), each
-// into the buffer its predecessor vacated.
+// Ping-pong: the work of a tile splits into a matrix phase M(t) -- the Q.K^T MFMAs of
+// tile t+1 and the P.V MFMAs of tile t -- and a vector phase V(t) -- mask, row max and
+// exp/pack of tile t+1.  Waves 0-3 and waves 4-7 (one of each on every SIMD) run the
+// same sequence one phase apart, with a workgroup barrier after every phase, so each
+// SIMD always has one wave on the matrix core and one on the vector ALU.
 //
 // Softmax bookkeeping per tile, for scale > 0: the max is taken over raw scores and the
 // scale is folded into one FMA per score, p = exp2(s*c - m*c) with c = scale*log2(e).
@@ -53,7 +54,11 @@
 namespace mi_attn {
 namespace {
 
-constexpr int kBN = 64;     // keys per tile
+constexpr int kBN = 64;                // keys per tile
+constexpr int kWaves = 8;              // two groups of four, one wave of each per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;       // query rows per workgroup
+constexpr int kCopyWaves = 4;          // the trailing group issues every tile copy
 constexpr float kRescaleSlack = 8.0f;  // log2 units the stale max may lag behind
 constexpr int kXcds = 8;               // accelerator complex dies (one L2 each) on MI355X
 
@@ -61,28 +66,19 @@ typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int D, int W>
-struct Geo {
-    static constexpr int CPR = D / 8;            // 16-byte chunks per row
-    static constexpr int KC = D / 16;            // MFMA k-steps of Q.K^T
-    static constexpr int DB = D / 32;            // 32-wide blocks of the output head dim
-    static constexpr int KS = CPR + 1;           // K row stride in chunks (padded)
-    static constexpr int NK = kBN * KS / 64;     // K copy instructions per tile
-    static constexpr int NKW = (NK + W - 1) / W; // ... per wave (at most)
-    static constexpr int NV = kBN * CPR / 64;    // V copy instructions per tile
-    static constexpr int NVW = NV / W;           // ... per wave
-    static constexpr int K_BYTES = kBN * KS * 16;
-    static constexpr int V_BYTES = kBN * CPR * 16;
-    static_assert(NV % W == 0, "V copies split evenly over the waves");
-};
-
-// V swizzle: XOR applied to the chunk index of row r (multiples of 4 chunks = 64 bytes).
 template <int D>
-__device__ __forceinline__ int vswz(int r) {
-    constexpr int QR = D / 32;        // 64-byte quarters per row
-    constexpr int RP = 4 / QR;        // rows per 256 bytes
-    return 4 * ((r / RP) & (QR - 1));
-}
+struct Geo {
+    static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+    static constexpr int KC = D / 16;                  // MFMA k-steps of Q.K^T
+    static constexpr int DB = D / 32;                  // 32-wide blocks of the output head dim
+    static constexpr int NK = 2 * KC;                  // K copy instructions per tile (1 KiB each)
+    static constexpr int NKW = (NK + kCopyWaves - 1) / kCopyWaves;
+    static constexpr int NV = 4 * DB;                  // V copy instructions per tile (1 KiB each)
+    static constexpr int NVW = (NV + kCopyWaves - 1) / kCopyWaves;
+    static constexpr int K_BYTES = kBN * D * 2;
+    static constexpr int V_BYTES = kBN * D * 2;
+    static_assert(NV % kCopyWaves == 0, "V copy rounds cover whole rows");
+};
 
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
@@ -95,7 +91,6 @@ __device__ __forceinline__ float halves_sum(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-
 
 // One 16-byte-per-lane copy from global memory straight into LDS: lane l reads
 // sbase + voff and its 16 bytes land at LDS address m0 + 16 * l (sbase and m0 are
@@ -117,290 +112,231 @@ __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70);
 // keeps it a branch instead of computing its body on every tile and selecting.
 __device__ __forceinline__ void keep_branch() { asm volatile("" ::); }
 
-template <int D, int RB, int W, bool POS_SCALE>
+template <int D, bool POS_SCALE>
 struct Prefill {
-    using G = Geo<D, W>;
+    using G = Geo<D>;
 
     // ---- per-lane constants ---------------------------------------------------------
     int lane, wave, g;
+    int cw;                     // index among the copying waves (group 1)
     int kvalid;                 // valid key rows of this item
     const char* kg;             // K rows of this (item, kv head)
     const char* vg;
     uint32_t k_lds0, v_lds0;    // LDS byte addresses of buffer 0
-    uint32_t koff[G::NKW];      // byte offsets of this lane's K copy chunks inside a tile
-    uint32_t voff;              // ... V (first copy; the others are +4096 bytes each)
-    int k_read;                 // LDS byte offset of this lane's K operand (row l%32, chunk g)
-    int v_read[G::DB];          // LDS byte offsets of this lane's transposing V reads
-    int lo_r[RB], hi_r[RB];     // this lane's key interval, per row block
-    bool blk_all_rows_valid[RB];
-    int b_inter_lo[RB], b_inter_hi[RB];  // keys every row of a row block sees
+    uint32_t k_off;             // byte offset of this lane's K copy chunk from a copy's base
+    uint32_t v_off;             // ... V
+    int lo_r, hi_r;             // this lane's key interval
+    bool all_rows_valid;
+    int inter_lo, inter_hi;     // keys every row of the wave sees
     float c2;                   // scale * log2(e)
 
     // ---- running state ----------------------------------------------------------------
-    bf16x8 qf[RB][G::KC];
-    f32x16 o[RB][G::DB];
-    float m_run[RB], l_run[RB];
+    bf16x8 qf[G::KC];
+    f32x16 o[G::DB];
+    f32x16 s[2];                // scores of the tile the next vector phase works on
+    bf16x8 pf[4];               // probabilities of the tile the next matrix phase uses
+    float m_run, l_run;
 
-    __device__ __forceinline__ void copy_k(int kt, int par) {
+    // K tile layout in LDS: 1 KiB block f = kb2*KC + kc holds, at 16*p, the chunk 2kc + p/32
+    // (dims 16kc + 8(p/32) + [0, 8)) of key 32*kb2 + p%32 -- exactly the MFMA A operand of
+    // lane p, so every K operand read is the lane-linear base + 16*lane.  Copy instruction
+    // f fills block f: lane p reads key 32kb2 + p%32 at chunk 2kc + p/32, i.e. a per-lane
+    // offset ((p%32)*D + 8*(p/32))*2 plus a per-copy base (32*kb2*D + 16*kc)*2.
+    __device__ __forceinline__ void copy_k(int kt, int par) const {
         const char* base = kg + (size_t)kt * kBN * D * 2;
         const bool tail = kt * kBN + kBN > kvalid;
 #pragma unroll
         for (int ii = 0; ii < G::NKW; ++ii) {
-            const int i = wave + W * ii;
-            if (i < G::NK) {
-                uint32_t off = koff[ii];
-                if (tail) {   // rows past the valid length repeat the last valid row
-                    const int p = i * 64 + lane;
-                    int row = p / G::KS, c = p - (p / G::KS) * G::KS;
-                    c = c < G::CPR ? c : 0;
-                    row = min(row, kvalid - 1 - kt * kBN);
-                    off = (uint32_t)((row * D + c * 8) * 2);
+            const int f = cw + kCopyWaves * ii;
+            if (f < G::NK) {
+                const int kb2 = f / G::KC, kc = f % G::KC;
+                const char* b = base + (32 * kb2 * D + 16 * kc) * 2;
+                uint32_t off = k_off;
+                if (tail) {
+                    // keys past the valid length repeat the last valid key; the clamped key
+                    // can lie before this block, so address from the tile base (kt < the
+                    // tile count guarantees kvalid - 1 - kt*64 >= 0)
+                    const int row = min(32 * kb2 + (lane & 31), kvalid - 1 - kt * kBN);
+                    b = base;
+                    off = (uint32_t)((row * D + 16 * kc + 8 * (lane >> 5)) * 2);
                 }
-                lds_dma16(base, off, k_lds0 + par * G::K_BYTES + i * 1024);
+                lds_dma16(b, off, k_lds0 + par * G::K_BYTES + f * 1024);
             }
         }
     }
 
-    __device__ __forceinline__ void copy_v(int kt, int par) {
+    // V tile layout in LDS: 512-byte block 2j + hi (j = c4*DB + db) holds, at 8*l, what
+    // lane l reads in the transposing read of V^T operand j, half hi: key
+    // 16c4 + 8hi + 4(l/32) + (l%16)/4, dims 32db + 16((l/16)%2) + 4(l%4) + [0, 4).  So both
+    // transposing reads are the lane-linear base + 8*lane (+512).  Copy instruction j fills
+    // blocks 2j, 2j+1; its 16-byte lane p (hi = p/32, q = p%32) takes key
+    // 16c4 + 8hi + 4(q/16) + (q%8)/2 at dims 32db + 16((q/8)%2) + 8(q%2) -- a per-lane
+    // offset plus a per-copy base (16c4*D + 32db)*2.
+    __device__ __forceinline__ void copy_v(int kt, int par) const {
         const char* base = vg + (size_t)kt * kBN * D * 2;
         const bool tail = kt * kBN + kBN > kvalid;
 #pragma unroll
         for (int ii = 0; ii < G::NVW; ++ii) {
-            const int i = wave + W * ii;
-            uint32_t off = voff;
-            const char* b = base + ii * (W * 1024);
-            if (tail) {
-                const int p = i * 64 + lane;
-                int row = p / G::CPR;
-                const int c = (p % G::CPR) ^ vswz<D>(row);
-                row = min(row, kvalid - 1 - kt * kBN);
-                off = (uint32_t)((row * D + c * 8) * 2);
-                b = base;
+            const int j = cw + kCopyWaves * ii;
+            if (j < G::NV) {
+                const int c4 = j / G::DB, db = j % G::DB;
+                const char* b = base + (16 * c4 * D + 32 * db) * 2;
+                uint32_t off = v_off;
+                if (tail) {   // as for K: clamp, and address from the tile base
+                    const int q = lane & 31;
+                    const int r = 8 * (lane >> 5) + 4 * (q >> 4) + ((q & 7) >> 1);
+                    const int row = min(16 * c4 + r, kvalid - 1 - kt * kBN);
+                    b = base;
+                    off = (uint32_t)((row * D + 32 * db + 16 * ((q >> 3) & 1) + 8 * (q & 1)) * 2);
+                }
+                lds_dma16(b, off, v_lds0 + par * G::V_BYTES + j * 1024);
             }
-            lds_dma16(b, off, v_lds0 + par * G::V_BYTES + i * 1024);
         }
     }
 
-    // K operand f of a tile (f = 32-key block * KC + k-step): row l%32 of the block,
+    // K operand f of a tile (32-key block f/KC, k-step f%KC): key l%32 of the block,
     // dims 16*kc + 8*g + [0, 8).
     __device__ __forceinline__ bf16x8 k_frag(const lds_char* kbuf, int f) const {
-        const int kb2 = f / G::KC, kc = f % G::KC;
-        return __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(kbuf + k_read + (kb2 * 32 * G::KS + 2 * kc) * 16));
+        return __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(kbuf + f * 1024 + lane * 16));
     }
 
     // V^T operand j of a tile (j = 16-key chunk * DB + 32-dim block) via two transposing
-    // reads.  Within 16-lane group G = lane/16, source lane s points at key
-    // 16*c4 + 4*g + s/4 (+8), dims 32*db + 16*(G%2) + 4*(s%4).
+    // reads.  Within 16-lane group G = lane/16, source lane s supplies key
+    // 16*c4 + 4*g + s/4 (+8 for the second read), dims 32*db + 16*(G%2) + 4*(s%4).
     __device__ __forceinline__ bf16x8 v_frag(const lds_char* vbuf, int j) const {
-        const int c4 = j / G::DB, db = j % G::DB;
-        const lds_char* p = vbuf + v_read[db] + 16 * c4 * 2 * D;
+        const lds_char* p = vbuf + j * 1024 + lane * 8;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * 2 * D));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 512));
         typedef __attribute__((ext_vector_type(8))) short s16x8;
         const s16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         return __builtin_bit_cast(bf16x8, vv);
     }
 
-    // Probabilities of one 16-key chunk u (row block u/4, chunk c4 = u%4 = block c4/2,
-    // elements 8*(c4%2) + [0, 8)) -> packed bf16 P^T operand, plus their fp32 row sums.
-    __device__ __forceinline__ void probs_chunk(const f32x16 (&s)[RB][2], bf16x8 (&pf)[RB][4], float (&ls)[RB][2],
-                                                const float (&m_use)[RB], int u) const {
-        const int rb = u / 4, c4 = u % 4;
-        u32x4 w;
-#pragma unroll
-        for (int jj = 0; jj < 8; jj += 2) {
-            const float s0 = s[rb][c4 / 2][8 * (c4 % 2) + jj], s1 = s[rb][c4 / 2][8 * (c4 % 2) + jj + 1];
-            const float p0 = POS_SCALE ? fast_exp2(fmaf(s0, c2, -m_use[rb])) : fast_exp2(s0 - m_use[rb]);
-            const float p1 = POS_SCALE ? fast_exp2(fmaf(s1, c2, -m_use[rb])) : fast_exp2(s1 - m_use[rb]);
-            w[jj / 2] = pack_bf16x2(p0, p1);
-            ls[rb][0] += p0;
-            ls[rb][1] += p1;
-        }
-        // anchor the operand here: left alone, the compiler sinks this side-effect-free
-        // work past the masking branch, next to the P.V products, away from the
-        // Q.K^T MFMAs it is meant to run beside
-        asm volatile("" : "+v"(w));
-        pf[rb][c4] = __builtin_bit_cast(bf16x8, w);
-    }
-
-    // S^T = K_tile . Q^T for every row block (the first tile, before the loop).
-    __device__ __forceinline__ void qk(f32x16 (&s)[RB][2], const lds_char* kbuf) const {
-#pragma unroll
-        for (int f = 0; f < 2 * G::KC; ++f) {
-            const int kb2 = f / G::KC, kc = f % G::KC;
-            const bf16x8 kf = k_frag(kbuf, f);
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-                s[rb][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[rb][kc], kc == 0 ? f32x16{} : s[rb][kb2], 0, 0, 0);
-        }
-    }
-
-    // First half of a pipelined step, as one explicitly ordered stream: the Q.K^T MFMAs
-    // of the next tile (each K operand read from LDS four steps ahead of its use and
-    // shared by all row blocks) with a slice of this tile's softmax after each of them.
-    // sched_barrier(0) keeps the compiler from regrouping the MFMAs.
-    template <bool HAS_NEXT>
-    __device__ __forceinline__ void qk_next_probs(f32x16 (&nxt)[RB][2], const f32x16 (&cur)[RB][2],
-                                                  bf16x8 (&pf)[RB][4], const lds_char* kbuf) {
+    // Matrix phase: S^T of the next tile (when there is one) from the K buffer, then
+    // O^T += V^T P^T of the current tile (when there is one) from the V buffer.  Operands
+    // are read from LDS a few MFMAs ahead of their use.
+    __device__ __forceinline__ void matrix_phase(bool do_qk, const lds_char* kbuf, bool do_pv, const lds_char* vbuf) {
         constexpr int NF = 2 * G::KC;   // K operands per tile
-        constexpr int NU = 4 * RB;      // softmax chunks
-        constexpr int PF = 4;           // K operands in flight
-        float m_use[RB], ls[RB][2];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            m_use[rb] = m_run[rb] == kNegInf ? 0.0f : m_run[rb];
-            ls[rb][0] = ls[rb][1] = 0.0f;
-        }
-        if constexpr (HAS_NEXT) {
+        constexpr int NJ = 4 * G::DB;   // V^T operands per tile
+
+        if (do_qk) {
+            constexpr int PF = 4;
             bf16x8 kf[PF];
+            // step f works on block kb2 = f%2, k-step kc = f/2: consecutive MFMAs alternate
+            // between the two accumulation chains
+            auto blk = [](int f) { return (f % 2) * G::KC + f / 2; };
 #pragma unroll
-            for (int f = 0; f < PF; ++f) kf[f] = k_frag(kbuf, f);
+            for (int f = 0; f < PF; ++f) kf[f] = k_frag(kbuf, blk(f));
 #pragma unroll
             for (int f = 0; f < NF; ++f) {
-                const int kb2 = f / G::KC, kc = f % G::KC;
+                const int kb2 = f % 2, kc = f / 2;
                 const bf16x8 k_now = kf[f % PF];
-                if (f + PF < NF) kf[f % PF] = k_frag(kbuf, f + PF);
+                if (f + PF < NF) kf[f % PF] = k_frag(kbuf, blk(f + PF));
+                s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_now, qf[kc], kc == 0 ? f32x16{} : s[kb2], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);   // keep the reads PF steps ahead, no further
+            }
+        }
+        if (do_pv) {
+            constexpr int PF = 3;
+            bf16x8 vf[PF];
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-                    nxt[rb][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_now, qf[rb][kc], kc == 0 ? f32x16{} : nxt[rb][kb2], 0, 0, 0);
+            for (int j = 0; j < PF; ++j) vf[j] = v_frag(vbuf, j);
 #pragma unroll
-                for (int u = f * NU / NF; u < (f + 1) * NU / NF; ++u) probs_chunk(cur, pf, ls, m_use, u);
+            for (int j = 0; j < NJ; ++j) {
+                const int c4 = j / G::DB, db = j % G::DB;
+                const bf16x8 v_now = vf[j % PF];
+                if (j + PF < NJ) vf[j % PF] = v_frag(vbuf, j + PF);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_now, pf[c4], o[db], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
-        } else {
-#pragma unroll
-            for (int u = 0; u < NU; ++u) probs_chunk(cur, pf, ls, m_use, u);
-        }
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            l_run[rb] += ls[rb][0] + ls[rb][1];
-            asm volatile("" : "+v"(l_run[rb]));
         }
     }
 
-    // Masks the scores of tile kt for rows that do not see every key of it (and scales
-    // them when the scale is not positive); element e of block kb2 is key
-    // kt*64 + 32*kb2 + 8*(e/4) + 4*g + e%4.
-    __device__ __forceinline__ void mask_scale(f32x16 (&s)[RB][2], int kt) const {
+    // Vector phase for tile kt (its scores are in s): mask the rows that do not see every
+    // key of it (scaling them when the scale is not positive), row max and lazy rescale,
+    // then probabilities -> packed bf16 P^T operands and the row sum.  Element e of block
+    // kb2 is key kt*64 + 32*kb2 + 8*(e/4) + 4*g + e%4; P chunk c4 (16 keys) = block c4/2,
+    // elements 8*(c4%2) + [0, 8).
+    __device__ __forceinline__ void vector_phase(int kt) {
+        // Issue priority: the other wave on this SIMD is in its matrix phase.  The vector
+        // phase is a dense stream of independent VALU instructions, and MFMAs issue through
+        // the same port; by age the vector wave would win it whenever it is the older one
+        // and starve the matrix core.  So this phase runs at priority 0 and hands the wave
+        // back priority 2 at its end -- before the barrier, so that the priority is already
+        // in place when the following matrix phase starts.
+        __builtin_amdgcn_s_setprio(0);
         const int kbase = kt * kBN;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            const bool full = blk_all_rows_valid[rb] && kbase >= b_inter_lo[rb] && kbase + kBN - 1 <= b_inter_hi[rb];
-            if (!full) {
-                keep_branch();
-                const int lo = lo_r[rb] - kbase - 4 * g, hi = hi_r[rb] - kbase - 4 * g;
-#pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int jj = 32 * kb2 + 8 * (e / 4) + (e % 4);
-                        if (!POS_SCALE) s[rb][kb2][e] *= c2;
-                        s[rb][kb2][e] = (jj >= lo && jj <= hi) ? s[rb][kb2][e] : kNegInf;
-                    }
-            } else if (!POS_SCALE) {
-#pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2) s[rb][kb2] *= c2;
-            }
-        }
-    }
-
-    // Running-max update from the per-lane partial maxima of a tile (log2 units after the
-    // scale), with the lazy rescale of O and l.
-    __device__ __forceinline__ void finish_max(float (&mx)[RB]) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            const float m = halves_max(mx[rb]);
-            const float m_tile = POS_SCALE ? m * c2 : m;
-            const bool need = m_tile > m_run[rb] + kRescaleSlack;
-            if (__builtin_amdgcn_ballot_w64(need)) {
-                keep_branch();
-                const float alpha = need ? fast_exp2(m_run[rb] - m_tile) : 1.0f;
-                m_run[rb] = need ? m_tile : m_run[rb];
-                l_run[rb] *= alpha;
-#pragma unroll
-                for (int i = 0; i < G::DB; ++i) o[rb][i] *= alpha;
-            }
-        }
-    }
-
-    // Row max of a whole (masked) score tile, then the running-max update.
-    __device__ __forceinline__ void update_max(const f32x16 (&s)[RB][2]) {
-        float mx[RB];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            mx[rb] = kNegInf;
+        const bool full = all_rows_valid && kbase >= inter_lo && kbase + kBN - 1 <= inter_hi;
+        if (!full) {
+            keep_branch();
+            const int lo = lo_r - kbase - 4 * g, hi = hi_r - kbase - 4 * g;
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-                for (int e = 0; e < 16; e += 2) mx[rb] = max3(mx[rb], s[rb][kb2][e], s[rb][kb2][e + 1]);
-        }
-        finish_max(mx);
-    }
-
-    // Second half of a pipelined step: this tile's P.V MFMAs (each V^T operand read two
-    // steps ahead and shared by all row blocks) with a slice of the next tile's row max
-    // after each of them; then the running-max update for the next tile.
-    template <bool HAS_NEXT>
-    __device__ __forceinline__ void pv_max_next(const bf16x8 (&pf)[RB][4], const lds_char* vbuf,
-                                                const f32x16 (&nxt)[RB][2]) {
-        constexpr int NJ = 4 * G::DB;   // V^T operands per tile
-        constexpr int NP = 16 * RB;     // max3 steps of the next tile
-        constexpr int PF = 2;           // V^T operands in flight
-        float mx[RB];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) mx[rb] = kNegInf;
-        bf16x8 vf[PF];
-#pragma unroll
-        for (int j = 0; j < PF; ++j) vf[j] = v_frag(vbuf, j);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int c4 = j / G::DB, db = j % G::DB;
-            const bf16x8 v_now = vf[j % PF];
-            if (j + PF < NJ) vf[j % PF] = v_frag(vbuf, j + PF);
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-                o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_now, pf[rb][c4], o[rb][db], 0, 0, 0);
-            if constexpr (HAS_NEXT) {
-#pragma unroll
-                for (int q = j * NP / NJ; q < (j + 1) * NP / NJ; ++q) {
-                    const int rb = q / 16, k = q % 16;
-                    mx[rb] = max3(mx[rb], nxt[rb][k / 8][2 * (k % 8)], nxt[rb][k / 8][2 * (k % 8) + 1]);
+                for (int e = 0; e < 16; ++e) {
+                    const int jj = 32 * kb2 + 8 * (e / 4) + (e % 4);
+                    if (!POS_SCALE) s[kb2][e] *= c2;
+                    s[kb2][e] = (jj >= lo && jj <= hi) ? s[kb2][e] : kNegInf;
                 }
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        } else if (!POS_SCALE) {
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] *= c2;
         }
-        if constexpr (HAS_NEXT) finish_max(mx);
-    }
-};
 
-// Launch shape per head dim: RB row blocks of 32 query rows per wave, W waves per
-// workgroup (sharing each K/V tile in LDS), MINB workgroups per CU.
-template <int D>
-struct Cfg {
-    static constexpr int RB = 1;
-    static constexpr int W = D == 128 ? 8 : 4;
-    static constexpr int THREADS = 64 * W;
-    static constexpr int BM = 32 * RB * W;          // query rows per workgroup
-    static constexpr int MINB = (RB == 1 && W == 4) ? 2 : 1;
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) mx = max3(mx, s[kb2][e], s[kb2][e + 1]);
+        mx = halves_max(mx);
+        const float m_tile = POS_SCALE ? mx * c2 : mx;
+        const bool need = m_tile > m_run + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            keep_branch();
+            const float alpha = need ? fast_exp2(m_run - m_tile) : 1.0f;
+            m_run = need ? m_tile : m_run;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < G::DB; ++i) o[i] *= alpha;
+        }
+
+        const float m_use = m_run == kNegInf ? 0.0f : m_run;
+        float ls0 = 0.0f, ls1 = 0.0f;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            u32x4 w;
+#pragma unroll
+            for (int jj = 0; jj < 8; jj += 2) {
+                const float s0 = s[c4 / 2][8 * (c4 % 2) + jj], s1 = s[c4 / 2][8 * (c4 % 2) + jj + 1];
+                const float p0 = POS_SCALE ? fast_exp2(fmaf(s0, c2, -m_use)) : fast_exp2(s0 - m_use);
+                const float p1 = POS_SCALE ? fast_exp2(fmaf(s1, c2, -m_use)) : fast_exp2(s1 - m_use);
+                w[jj / 2] = pack_bf16x2(p0, p1);
+                ls0 += p0;
+                ls1 += p1;
+            }
+            pf[c4] = __builtin_bit_cast(bf16x8, w);
+        }
+        l_run += ls0 + ls1;
+        __builtin_amdgcn_s_setprio(2);
+    }
 };
 
 template <int D, bool POS_SCALE>
-__global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_kernel(PrefillArgs a) {
-    constexpr int RB = Cfg<D>::RB;
-    constexpr int W = Cfg<D>::W;
-    constexpr int BM = Cfg<D>::BM;
-    using G = Geo<D, W>;
-    __shared__ __attribute__((aligned(16))) u32x4 k_lds[2][kBN * G::KS];
+__global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a) {
+    using G = Geo<D>;
+    __shared__ __attribute__((aligned(16))) u32x4 k_lds[2][kBN * G::CPR];
     __shared__ __attribute__((aligned(16))) u32x4 v_lds[2][kBN * G::CPR];
 
-    Prefill<D, RB, W, POS_SCALE> st;
+    Prefill<D, POS_SCALE> st;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5;                  // half of the wave
+    const int grp = wave / 4;                 // ping-pong group: 0 leads, 1 trails a phase
     st.lane = lane;
     st.wave = wave;
     st.g = g;
+    st.cw = wave - 4;
     // One-dimensional grid, q-tile slowest: for causal attention the tiles near the end of
     // the sequence carry the most keys, so the whole grid runs longest-first and the short
     // tiles fill in at the end instead of leaving a tail of long ones.
@@ -408,17 +344,17 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_ke
     // own L2.  When the (item, kv head) units divide evenly, every XCD gets whole units --
     // all query heads of a kv head -- so that a unit's K/V tiles are fetched into one L2
     // and reused there by all its query heads.
-    const int grp = a.q_heads / a.kv_heads;
+    const int qgrp = a.q_heads / a.kv_heads;
     const int units = a.batch * a.kv_heads;
     int qt_rank, b, h;
     if (units % kXcds == 0) {
         const int xcd = (int)(blockIdx.x % kXcds), k = (int)(blockIdx.x / kXcds);
         const int per_xcd = units / kXcds;
-        const int hig = k % grp;
-        const int unit = ((k / grp) % per_xcd) * kXcds + xcd;
-        qt_rank = k / (grp * per_xcd);
+        const int hig = k % qgrp;
+        const int unit = ((k / qgrp) % per_xcd) * kXcds + xcd;
+        qt_rank = k / (qgrp * per_xcd);
         b = unit / a.kv_heads;
-        h = (unit % a.kv_heads) * grp + hig;
+        h = (unit % a.kv_heads) * qgrp + hig;
     } else {
         const int bh = (int)(blockIdx.x % (unsigned)(a.batch * a.q_heads));
         qt_rank = (int)(blockIdx.x / (unsigned)(a.batch * a.q_heads));
@@ -426,14 +362,14 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_ke
         h = bh % a.q_heads;
     }
     const int qt = a.causal ? (a.n_qtiles - 1 - qt_rank) : qt_rank;
-    const int kvh = h / grp;
+    const int kvh = h / qgrp;
 
     int valid = a.kv_len;
     if (a.seq_lens) valid = min(max(a.seq_lens[b], 0), a.kv_len);
     st.kvalid = valid;
 
-    const int q0 = qt * BM;
-    const int last_row = min(q0 + BM, a.q_len) - 1;
+    const int q0 = qt * kBM;
+    const int last_row = min(q0 + kBM, a.q_len) - 1;
     const int half_w = a.window / 2;
 
     // ---- key range of the whole workgroup -------------------------------------------
@@ -454,13 +390,11 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_ke
     const int kt_begin = k_begin / kBN;
     const int kt_end = k_end > k_begin ? (k_end + kBN - 1) / kBN : kt_begin;
 
-    // ---- per row block: this lane's query row and key interval, the block's common keys
-    int my_row[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int r0 = q0 + (wave * RB + rb) * 32;
-        my_row[rb] = r0 + (lane & 31);
-        const int my_pos = a.pos_offset + my_row[rb];
+    // ---- this lane's query row and key interval, the wave's common keys ----------------
+    const int r0 = q0 + wave * 32;
+    const int my_row = r0 + (lane & 31);
+    {
+        const int my_pos = a.pos_offset + my_row;
         int lo_r = 0, hi_r = valid - 1;
         if (a.causal) hi_r = min(hi_r, my_pos);
         if (a.window > 0) {
@@ -471,9 +405,9 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_ke
                 hi_r = min(hi_r, my_pos + half_w);
             }
         }
-        if (my_pos >= valid || my_row[rb] >= a.q_len) hi_r = -1;
-        st.lo_r[rb] = lo_r;
-        st.hi_r[rb] = hi_r;
+        if (my_pos >= valid || my_row >= a.q_len) hi_r = -1;
+        st.lo_r = lo_r;
+        st.hi_r = hi_r;
 
         const int r1 = min(r0 + 31, a.q_len - 1);
         const int bp_lo = a.pos_offset + r0, bp_hi = a.pos_offset + r1;
@@ -487,25 +421,24 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_ke
                 inter_hi = min(inter_hi, bp_lo + half_w);
             }
         }
-        st.b_inter_lo[rb] = inter_lo;
-        st.b_inter_hi[rb] = inter_hi;
-        st.blk_all_rows_valid[rb] = r0 < a.q_len && bp_hi < valid;
+        st.inter_lo = inter_lo;
+        st.inter_hi = inter_hi;
+        st.all_rows_valid = r0 < a.q_len && bp_hi < valid;
     }
 
-    // ---- Q^T operands: lane l holds row l%32 of each block, dims 16*kc + 8*g + [0, 8)
+    // ---- Q^T operand: lane l holds row l%32, dims 16*kc + 8*g + [0, 8) ---------------
     const size_t q_head = ((size_t)b * a.q_heads + h) * (size_t)a.q_len;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const uint16_t* qrow = (const uint16_t*)a.q + (q_head + (size_t)min(my_row[rb], a.q_len - 1)) * D;
-        const bool in = my_row[rb] < a.q_len;
+    {
+        const uint16_t* qrow = (const uint16_t*)a.q + (q_head + (size_t)min(my_row, a.q_len - 1)) * D;
+        const bool in = my_row < a.q_len;
 #pragma unroll
         for (int kc = 0; kc < G::KC; ++kc) {
             u32x4 w = in ? *(const u32x4*)(qrow + 16 * kc + 8 * g) : u32x4{0, 0, 0, 0};
-            st.qf[rb][kc] = __builtin_bit_cast(bf16x8, w);
+            st.qf[kc] = __builtin_bit_cast(bf16x8, w);
         }
     }
     // Q must have arrived before any copy is in flight: otherwise the compiler's own wait
-    // for Q inside the loop would be a vmcnt(0) that also waits for the next tile's copy
+    // for Q later on would be a vmcnt(0) that also waits for tile copies
     wait_vm0();
 
     const size_t kv_head = ((size_t)b * a.kv_heads + kvh) * (size_t)a.kv_len;
@@ -513,103 +446,97 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_ke
     st.vg = (const char*)((const uint16_t*)a.v + kv_head * D);
     st.k_lds0 = lds_addr(k_lds[0]);
     st.v_lds0 = lds_addr(v_lds[0]);
-#pragma unroll
-    for (int ii = 0; ii < G::NKW; ++ii) {
-        const int p = (wave + W * ii) * 64 + lane;
-        const int row = p / G::KS;
-        int c = p - row * G::KS;
-        c = c < G::CPR ? c : 0;
-        st.koff[ii] = (uint32_t)((row * D + c * 8) * 2);
-    }
+    st.k_off = (uint32_t)(((lane & 31) * D + 8 * (lane >> 5)) * 2);
     {
-        const int p = wave * 64 + lane;
-        const int row = p / G::CPR;
-        const int c = (p % G::CPR) ^ vswz<D>(row);
-        st.voff = (uint32_t)((row * D + c * 8) * 2);
-    }
-    st.k_read = ((lane & 31) * G::KS + g) * 16;
-    {
-        const int r = 4 * g + ((lane & 15) >> 2);
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db) {
-            const int cb = 64 * db + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);   // column byte
-            st.v_read[db] = r * 2 * D + 16 * ((cb >> 4) ^ vswz<D>(r)) + (cb & 15);
-        }
+        const int q = lane & 31;
+        const int r = 8 * (lane >> 5) + 4 * (q >> 4) + ((q & 7) >> 1);
+        st.v_off = (uint32_t)((r * D + 16 * ((q >> 3) & 1) + 8 * (q & 1)) * 2);
     }
     st.c2 = a.scale * kLog2e;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-        for (int i = 0; i < G::DB; ++i) st.o[rb][i] = f32x16{};
-        st.m_run[rb] = kNegInf;   // running (possibly stale) max of this lane's row, log2 units
-        st.l_run[rb] = 0.0f;      // running sum over this lane's half of the keys
-    }
+    for (int i = 0; i < G::DB; ++i) st.o[i] = f32x16{};
+    st.m_run = kNegInf;    // running (possibly stale) max of this lane's row, log2 units
+    st.l_run = 0.0f;       // running sum over this lane's half of the keys
 
-    const lds_char* kb[2] = {(const lds_char*)(const void*)k_lds[0], (const lds_char*)(const void*)k_lds[1]};
-    const lds_char* vb[2] = {(const lds_char*)(const void*)v_lds[0], (const lds_char*)(const void*)v_lds[1]};
-
-    // One pipelined step for tile kt = kt_begin + j (buffer parity PAR = j & 1): cur holds
-    // the masked scores of tile kt with the running max already updated for it.
-    auto step = [&](auto has_next_c, auto par_c, f32x16 (&cur)[RB][2], f32x16 (&nxt)[RB][2], int j) {
-        constexpr bool HAS_NEXT = decltype(has_next_c)::value;
-        constexpr int PAR = decltype(par_c)::value;
-        const int kt = kt_begin + j;
-        wait_vm0();          // this thread's copies of K(kt+1) and V(kt) have landed
-        __syncthreads();     // ... everyone's; and nobody still reads K(kt) or V(kt-1)
-        if (kt + 2 < kt_end) st.copy_k(kt + 2, PAR);
-        if (HAS_NEXT) st.copy_v(kt + 1, PAR ^ 1);
-        bf16x8 pf[RB][4];
-        st.template qk_next_probs<HAS_NEXT>(nxt, cur, pf, kb[PAR ^ 1]);
-        if (HAS_NEXT) st.mask_scale(nxt, kt + 1);
-        st.template pv_max_next<HAS_NEXT>(pf, vb[PAR], nxt);
-    };
-
+    // ---- the phase sequence ------------------------------------------------------------
+    // With n tiles (relative index t = 0..n-1) a wave runs M(-1) V(-1) M(0) V(0) ... M(n-1):
+    // M(t) = S of tile t+1 (if t+1 < n) and O += P V of tile t (if t >= 0), V(t) = vector
+    // phase of tile t+1 (if t+1 < n).  Group 0 runs phase p in slot p, group 1 in slot
+    // p+1; every slot ends with a workgroup barrier (2n+3 slots in all).
+    // Tiles: K(t+1) and V(t) are read in slots 2t+2 and 2t+3.  For t >= 1 they are copied
+    // in slot 2t (into the buffers of K(t-1) and V(t-2), last read in slot 2t-1) and
+    // waited for at the end of slot 2t+1; K(0), V(0) and K(1) are copied before slot 0.
     const int n = kt_end - kt_begin;
-    if (n > 0) {
-        f32x16 sa[RB][2], sb[RB][2];
-        st.copy_k(kt_begin, 0);
-        wait_vm0();
+    const lds_char* kb0 = (const lds_char*)(const void*)k_lds[0];
+    const lds_char* vb0 = (const lds_char*)(const void*)v_lds[0];
+    auto kbuf = [&](int t) { return kb0 + (t & 1) * G::K_BYTES; };
+    auto vbuf = [&](int t) { return vb0 + (t & 1) * G::V_BYTES; };
+    auto copies = [&](int t) {   // the copies of even slot 2t (t >= 1), issued by group 1
+        if (t + 1 < n) st.copy_k(kt_begin + t + 1, (t + 1) & 1);
+        if (t < n) st.copy_v(kt_begin + t, t & 1);
+    };
+    auto slot_end = [&](bool odd) {
+        if (odd) wait_vm0();   // this wave's copies of the previous slot have landed
         __syncthreads();
-        if (n > 1) st.copy_k(kt_begin + 1, 1);
-        st.copy_v(kt_begin, 0);
-        st.qk(sa, kb[0]);
-        st.mask_scale(sa, kt_begin);
-        st.update_max(sa);
-        typedef std::integral_constant<bool, true> T_;
-        typedef std::integral_constant<bool, false> F_;
-        typedef std::integral_constant<int, 0> P0;
-        typedef std::integral_constant<int, 1> P1;
-        int j = 0;
-        for (; j + 2 < n; j += 2) {
-            step(T_{}, P0{}, sa, sb, j);
-            step(T_{}, P1{}, sb, sa, j + 1);
+    };
+    if (n > 0) {
+        __builtin_amdgcn_s_setprio(2);   // matrix phases run at priority 2, vector phases at 0
+        if (grp == 1) {
+            st.copy_k(kt_begin, 0);
+            st.copy_v(kt_begin, 0);
+            if (n > 1) st.copy_k(kt_begin + 1, 1);
+            wait_vm0();
         }
-        if (j + 1 < n) {
-            step(T_{}, P0{}, sa, sb, j);
-            step(F_{}, P1{}, sb, sa, j + 1);
+        __syncthreads();
+        if (grp == 0) {
+            st.matrix_phase(true, kbuf(0), false, vbuf(0));           // slot 0: M(-1)
+            slot_end(false);
+            st.vector_phase(kt_begin);                                 // slot 1: V(-1)
+            slot_end(true);
+            for (int t = 0; t + 1 < n; ++t) {
+                st.matrix_phase(true, kbuf(t + 1), true, vbuf(t));     // slot 2t+2: M(t)
+                slot_end(false);
+                st.vector_phase(kt_begin + t + 1);                     // slot 2t+3: V(t)
+                slot_end(true);
+            }
+            st.matrix_phase(false, kbuf(0), true, vbuf(n - 1));        // slot 2n: M(n-1)
+            slot_end(false);
+            slot_end(true);                                            // slot 2n+1
+            slot_end(false);                                           // slot 2n+2
         } else {
-            step(F_{}, P0{}, sa, sb, j);
+            slot_end(false);                                           // slot 0
+            st.matrix_phase(true, kbuf(0), false, vbuf(0));           // slot 1: M(-1)
+            slot_end(true);
+            copies(1);                                                 // slot 2: V(-1)
+            st.vector_phase(kt_begin);
+            slot_end(false);
+            for (int t = 0; t + 1 < n; ++t) {
+                st.matrix_phase(true, kbuf(t + 1), true, vbuf(t));     // slot 2t+3: M(t)
+                slot_end(true);
+                copies(t + 2);                                         // slot 2t+4: V(t)
+                st.vector_phase(kt_begin + t + 1);
+                slot_end(false);
+            }
+            st.matrix_phase(false, kbuf(0), true, vbuf(n - 1));        // slot 2n+1: M(n-1)
+            slot_end(true);
+            slot_end(false);                                           // slot 2n+2
         }
     }
 
     // ---- epilogue: normalise, zero padded / empty rows, store bf16 --------------------
+    const float l_tot = halves_sum(st.l_run);
+    if (my_row >= a.q_len) return;
+    const float inv = (st.hi_r >= 0 && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
+    uint16_t* orow = (uint16_t*)a.out + (q_head + (size_t)my_row) * D;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const float l_tot = halves_sum(st.l_run[rb]);
-        if (my_row[rb] < a.q_len) {
-            const float inv = (st.hi_r[rb] >= 0 && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
-            uint16_t* orow = (uint16_t*)a.out + (q_head + (size_t)my_row[rb]) * D;
+    for (int db = 0; db < G::DB; ++db) {
 #pragma unroll
-            for (int db = 0; db < G::DB; ++db) {
-#pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const int d = 32 * db + 8 * e4 + 4 * g;
-                    u32x2 w;
-                    w[0] = pack_bf16x2(st.o[rb][db][4 * e4] * inv, st.o[rb][db][4 * e4 + 1] * inv);
-                    w[1] = pack_bf16x2(st.o[rb][db][4 * e4 + 2] * inv, st.o[rb][db][4 * e4 + 3] * inv);
-                    *(u32x2*)(orow + d) = w;
-                }
-            }
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const int d = 32 * db + 8 * e4 + 4 * g;
+            u32x2 w;
+            w[0] = pack_bf16x2(st.o[db][4 * e4] * inv, st.o[db][4 * e4 + 1] * inv);
+            w[1] = pack_bf16x2(st.o[db][4 * e4 + 2] * inv, st.o[db][4 * e4 + 3] * inv);
+            *(u32x2*)(orow + d) = w;
         }
     }
 }
@@ -617,12 +544,12 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_ke
 template <int D>
 hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
     PrefillArgs args = a;
-    args.n_qtiles = (a.q_len + Cfg<D>::BM - 1) / Cfg<D>::BM;
+    args.n_qtiles = (a.q_len + kBM - 1) / kBM;
     const dim3 grid((unsigned)args.n_qtiles * a.q_heads * a.batch);
     if (args.scale > 0.0f)
-        hipLaunchKernelGGL((prefill_bf16_kernel<D, true>), grid, dim3(Cfg<D>::THREADS), 0, stream, args);
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, true>), grid, dim3(kThreads), 0, stream, args);
     else
-        hipLaunchKernelGGL((prefill_bf16_kernel<D, false>), grid, dim3(Cfg<D>::THREADS), 0, stream, args);
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, false>), grid, dim3(kThreads), 0, stream, args);
     return hipGetLastError();
 }
 
@@ -630,8 +557,8 @@ hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, hipStream_t stream) {
     switch (head_dim) {
-        case 32: return launch_d<32>(a, stream);
-        case 64: return launch_d<64>(a, stream);
+        case 32:
+        case 64: return launch_prefill_bf16_narrow(a, head_dim, stream);
         case 128: return launch_d<128>(a, stream);
         default: return hipErrorInvalidValue;
     }
