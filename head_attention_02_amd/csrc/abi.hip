@@ -93,6 +93,7 @@ size_t attn_decode_workspace_bytes(int batch, int q_heads, int kv_heads, int kv_
         !supported_head_dim(head_dim))
         return 0;
     const mi_attn::DecodePlan p = mi_attn::plan_decode(batch, q_heads, kv_heads, kv_len, head_dim);
+    if (p.splits == 1) return 0;   // one workgroup per key range writes the output itself
     return (size_t)batch * q_heads * p.splits * (head_dim + 2) * sizeof(float);
 }
 

@@ -31,11 +31,13 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_workspace_query():
-    n = mi.attn_decode_workspace_bytes(64, 32, 8, 8192, 128)
-    assert n > 0 and n % 4 == 0
-    # one fp32 partial state (head_dim + 2 values) per (item, query head, split)
-    per_split = 64 * 32 * (128 + 2) * 4
-    assert n % per_split == 0
+    # few (item, kv head) units: the key range is split, one fp32 partial state
+    # (head_dim + 2 values) per (item, query head, split)
+    n = mi.attn_decode_workspace_bytes(2, 32, 8, 8192, 128)
+    per_split = 2 * 32 * (128 + 2) * 4
+    assert n > per_split and n % per_split == 0
+    # enough units to fill the GPU without splitting: no workspace at all
+    assert mi.attn_decode_workspace_bytes(64, 32, 8, 8192, 128) == 0
     assert mi.attn_decode_workspace_bytes(0, 32, 8, 8192, 128) == 0
     assert mi.attn_decode_workspace_bytes(64, 30, 8, 8192, 128) == 0
     assert mi.attn_decode_workspace_bytes(64, 32, 8, 8192, 96) == 0
@@ -91,8 +93,9 @@ def test_prefill_empty_calls_are_ok_without_a_gpu():
     (dict(pos_offset=16), mi.MI_ATTN_ERR_INVALID, "pos_offset"),
     (dict(window=-1), mi.MI_ATTN_ERR_INVALID, "negative"),
     (dict(head_dim=48), mi.MI_ATTN_ERR_UNSUPPORTED, "head_dim 48"),
-    (dict(ws_bytes=16), mi.MI_ATTN_ERR_INVALID, "workspace"),
-    (dict(ws=None), mi.MI_ATTN_ERR_INVALID, "workspace"),
+    # 4096 keys of 4 (item, kv head) units are split, so a workspace is needed
+    (dict(kv_len=4096, capacity=4096, ws_bytes=16), mi.MI_ATTN_ERR_INVALID, "workspace"),
+    (dict(kv_len=4096, capacity=4096, ws=None), mi.MI_ATTN_ERR_INVALID, "workspace"),
     (dict(v=None), mi.MI_ATTN_ERR_INVALID, "null"),
 ])
 def test_decode_validation(kw, status, msg):

@@ -104,6 +104,9 @@ DECODE_CASES = [
     (2, 8, 1, 333, 333, 128, 332, None, 1, "bf16"),
     (2, 4, 1, 300, 300, 128, 299, None, 17, "f32"),
     (2, 6, 2, 256, 200, 64, 0, [200, 50], 0, "f32"),
+    # 512 (item, kv head) units: one workgroup per key range, no split and no combine pass
+    (64, 8, 8, 96, 90, 64, 0, [(37 * i) % 91 for i in range(64)], 0, "f32"),
+    (128, 8, 4, 64, 64, 128, 40, None, 9, "bf16"),
 ]
 
 
