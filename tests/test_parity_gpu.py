@@ -65,6 +65,12 @@ PREFILL_CASES = [
     (1, 2, 2, 70, 90, 128, False, 20, [85], 9, "f32"),
     (1, 4, 4, 100, 100, 32, True, 0, None, 16, "f32"),
     (3, 3, 1, 65, 65, 128, False, 0, [65, 0, 13], 0, "f32"),
+    # several 256-row q-tiles at head dim 128, bidirectional, banded, and with the
+    # (item, kv head) unit count a multiple of 8 (the XCD-grouped block order)
+    (1, 8, 2, 520, 700, 128, False, 0, None, 0, "bf16"),
+    (1, 4, 2, 600, 600, 128, False, 0, None, 200, "bf16"),
+    (2, 8, 4, 300, 300, 128, True, 0, None, 0, "bf16"),
+    (2, 8, 4, 300, 300, 64, True, 0, [300, 257], 0, "bf16"),
 ]
 
 
@@ -125,6 +131,20 @@ def test_decode_parity(mi, ref, case):
     import torch
     torch.cuda.synchronize()
     check(to_f64(got), want, dt, f"decode {case}")
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("scale", [0.0, -0.2])
+def test_prefill_nonpositive_scale(mi, ref, D, scale):
+    """scale <= 0 takes the kernels' other softmax form (scale applied before the max);
+    scale 0 makes every visible key equally likely."""
+    say(f"prefill scale {scale} D {D}")
+    x = W.random_prefill(13, 2, 4, 2, 270, 270, D, "bf16")
+    want = ref.prefill(x["q"], x["k"], x["v"], scale=scale, causal=True, window=100)
+    got = mi.attn_prefill(to_gpu(x["q"]), to_gpu(x["k"]), to_gpu(x["v"]), causal=True, window=100, scale=scale)
+    import torch
+    torch.cuda.synchronize()
+    check(to_f64(got), want, "bf16", f"scale {scale} D {D}")
 
 
 # ---------------------------------------------------------------------------
