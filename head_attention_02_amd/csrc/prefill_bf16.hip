@@ -437,9 +437,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
             st.qf[kc] = __builtin_bit_cast(bf16x8, w);
         }
     }
-    // Q must have arrived before any copy is in flight: otherwise the compiler's own wait
-    // for Q later on would be a vmcnt(0) that also waits for tile copies
-    wait_vm0();
+    // Q is waited for in the prologue below, together with the first tile copies (one
+    // memory latency instead of two).  That explicit wait also keeps the compiler from
+    // placing its own wait for Q inside the loop, where it would also wait for the tile
+    // copies in flight.
 
     const size_t kv_head = ((size_t)b * a.kv_heads + kvh) * (size_t)a.kv_len;
     st.kg = (const char*)((const uint16_t*)a.k + kv_head * D);
@@ -485,8 +486,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
             st.copy_k(kt_begin, 0);
             st.copy_v(kt_begin, 0);
             if (n > 1) st.copy_k(kt_begin + 1, 1);
-            wait_vm0();
         }
+        wait_vm0();   // Q, and group 1's first tile copies, have landed
         __syncthreads();
         if (grp == 0) {
             st.matrix_phase(true, kbuf(0), false, vbuf(0));           // slot 0: M(-1)
