@@ -494,9 +494,10 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
             st.qf[rb][kc] = __builtin_bit_cast(bf16x8, w);
         }
     }
-    // Q must have arrived before any copy is in flight: otherwise the compiler's own wait
-    // for Q inside the loop would be a vmcnt(0) that also waits for the next tile's copy
-    wait_vm0();
+    // Q is waited for in the prologue below, together with the first tile copies (one
+    // memory latency instead of several).  That explicit wait also keeps the compiler from
+    // placing its own wait for Q inside the loop, where it would also wait for the next
+    // tile's copy.
 
     const size_t kv_head = ((size_t)b * a.kv_heads + kvh) * (size_t)a.kv_len;
     st.kg = (const char*)((const uint16_t*)a.k + kv_head * D);
@@ -558,10 +559,10 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
     if (n > 0) {
         f32x16 sa[RB][2], sb[RB][2];
         st.copy_k(kt_begin, 0);
-        wait_vm0();
-        __syncthreads();
         if (n > 1) st.copy_k(kt_begin + 1, 1);
         st.copy_v(kt_begin, 0);
+        wait_vm0();          // Q, K(0), K(1) and V(0) have landed
+        __syncthreads();
         st.qk(sa, kb[0]);
         st.mask_scale(sa, kt_begin);
         st.update_max(sa);
