@@ -128,6 +128,7 @@ struct Prefill {
     int lo_r, hi_r;             // this lane's key interval
     bool all_rows_valid;
     int inter_lo, inter_hi;     // keys every row of the wave sees
+    int union_lo, union_hi;     // keys some row of the wave sees (a superset; empty if hi < lo)
     float c2;                   // scale * log2(e)
 
     // ---- running state ----------------------------------------------------------------
@@ -215,6 +216,13 @@ struct Prefill {
     // Matrix phase: S^T of the next tile (when there is one) from the K buffer, then
     // O^T += V^T P^T of the current tile (when there is one) from the V buffer.  Operands
     // are read from LDS a few MFMAs ahead of their use.
+    // Whether key tile kt holds a key that some row of this wave sees.  Tiles that hold
+    // none (the far side of the causal diagonal, outside the band) take no MFMA and no
+    // softmax work in this wave; the other waves of the workgroup still need them.
+    __device__ __forceinline__ bool wave_sees(int kt) const {
+        return kt * kBN <= union_hi && kt * kBN + kBN - 1 >= union_lo;
+    }
+
     __device__ __forceinline__ void matrix_phase(bool do_qk, const lds_char* kbuf, bool do_pv, const lds_char* vbuf) {
         constexpr int NF = 2 * G::KC;   // K operands per tile
         constexpr int NJ = 4 * G::DB;   // V^T operands per tile
@@ -265,6 +273,10 @@ struct Prefill {
         // back priority 2 at its end -- before the barrier, so that the priority is already
         // in place when the following matrix phase starts.
         __builtin_amdgcn_s_setprio(0);
+        if (!wave_sees(kt)) {   // no score of this tile was computed, and none is used
+            __builtin_amdgcn_s_setprio(2);
+            return;
+        }
         const int kbase = kt * kBN;
         const bool full = all_rows_valid && kbase >= inter_lo && kbase + kBN - 1 <= inter_hi;
         if (!full) {
@@ -423,6 +435,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
         }
         st.inter_lo = inter_lo;
         st.inter_hi = inter_hi;
+        int union_lo = 0, union_hi = valid - 1;
+        if (a.causal) union_hi = min(union_hi, bp_hi);
+        if (a.window > 0) {
+            if (a.causal) {
+                union_lo = max(0, bp_lo - a.window + 1);
+            } else {
+                union_lo = max(0, bp_lo - half_w);
+                union_hi = min(union_hi, bp_hi + half_w);
+            }
+        }
+        if (r0 >= a.q_len || bp_lo >= valid) union_hi = -1;   // no row of the wave is a query
+        st.union_lo = union_lo;
+        st.union_hi = union_hi;
         st.all_rows_valid = r0 < a.q_len && bp_hi < valid;
     }
 
@@ -490,35 +515,35 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
         wait_vm0();   // Q, and group 1's first tile copies, have landed
         __syncthreads();
         if (grp == 0) {
-            st.matrix_phase(true, kbuf(0), false, vbuf(0));           // slot 0: M(-1)
+            st.matrix_phase(st.wave_sees(kt_begin), kbuf(0), false, vbuf(0));           // slot 0: M(-1)
             slot_end(false);
             st.vector_phase(kt_begin);                                 // slot 1: V(-1)
             slot_end(true);
             for (int t = 0; t + 1 < n; ++t) {
-                st.matrix_phase(true, kbuf(t + 1), true, vbuf(t));     // slot 2t+2: M(t)
+                st.matrix_phase(st.wave_sees(kt_begin + t + 1), kbuf(t + 1), st.wave_sees(kt_begin + t), vbuf(t));     // slot 2t+2: M(t)
                 slot_end(false);
                 st.vector_phase(kt_begin + t + 1);                     // slot 2t+3: V(t)
                 slot_end(true);
             }
-            st.matrix_phase(false, kbuf(0), true, vbuf(n - 1));        // slot 2n: M(n-1)
+            st.matrix_phase(false, kbuf(0), st.wave_sees(kt_begin + n - 1), vbuf(n - 1));        // slot 2n: M(n-1)
             slot_end(false);
             slot_end(true);                                            // slot 2n+1
             slot_end(false);                                           // slot 2n+2
         } else {
             slot_end(false);                                           // slot 0
-            st.matrix_phase(true, kbuf(0), false, vbuf(0));           // slot 1: M(-1)
+            st.matrix_phase(st.wave_sees(kt_begin), kbuf(0), false, vbuf(0));           // slot 1: M(-1)
             slot_end(true);
             copies(1);                                                 // slot 2: V(-1)
             st.vector_phase(kt_begin);
             slot_end(false);
             for (int t = 0; t + 1 < n; ++t) {
-                st.matrix_phase(true, kbuf(t + 1), true, vbuf(t));     // slot 2t+3: M(t)
+                st.matrix_phase(st.wave_sees(kt_begin + t + 1), kbuf(t + 1), st.wave_sees(kt_begin + t), vbuf(t));     // slot 2t+3: M(t)
                 slot_end(true);
                 copies(t + 2);                                         // slot 2t+4: V(t)
                 st.vector_phase(kt_begin + t + 1);
                 slot_end(false);
             }
-            st.matrix_phase(false, kbuf(0), true, vbuf(n - 1));        // slot 2n+1: M(n-1)
+            st.matrix_phase(false, kbuf(0), st.wave_sees(kt_begin + n - 1), vbuf(n - 1));        // slot 2n+1: M(n-1)
             slot_end(true);
             slot_end(false);                                           // slot 2n+2
         }
