@@ -141,6 +141,49 @@ class Oracle:
         self.threads_used = ret
         return out
 
+    # ---- per-item caches and the cache append ------------------------------------
+    # ferrum-kernels `Backend` page, Provided Methods: `kv_cache_append_batched_per_cache`
+    # writes item i's new head-major row [nkv, hd] into its own cache [nkv, capacity, hd]
+    # at the offset cache_lens[i]; `flash_attention_batched_per_cache` attends M items'
+    # queries over their own caches with per-item lengths, replacing M single-item calls.
+
+    @staticmethod
+    def append(k_caches, v_caches, k_new, v_new, cache_lens):
+        """Caches after appending one token per item: lists of `B` arrays
+        [Hkv, capacity, D] (copies; the inputs are not modified).  Row cache_lens[b] of
+        every kv head of item b becomes k_new[b] / v_new[b].  An item whose offset lies
+        outside [0, capacity) has no room and keeps its caches unchanged."""
+        ko = [np.array(c, copy=True) for c in k_caches]
+        vo = [np.array(c, copy=True) for c in v_caches]
+        for b, n in enumerate(np.asarray(cache_lens, dtype=np.int64)):
+            cap = ko[b].shape[1]
+            if 0 <= n < cap:
+                ko[b][:, n, :] = k_new[b]
+                vo[b][:, n, :] = v_new[b]
+        return ko, vo
+
+    def decode_per_cache(self, q, k_caches, v_caches, kv_lens, *, scale: float, window: int = 0,
+                         rows=None, nthreads: int | None = None) -> np.ndarray:
+        """q [B,Hq,D]; k_caches / v_caches: `B` arrays [Hkv, capacity, D], one per item;
+        item b has kv_lens[b] keys and its query at kv_lens[b] - 1.  This is the batched
+        decode over the items' caches side by side."""
+        K = np.stack([np.asarray(c) for c in k_caches])
+        V = np.stack([np.asarray(c) for c in v_caches])
+        return self.decode(q, K, V, kv_len=K.shape[2], scale=scale, kv_lens=kv_lens, window=window, rows=rows,
+                           nthreads=nthreads)
+
+    def decode_append(self, q, k_new, v_new, k_caches, v_caches, cache_lens, *, scale: float, window: int = 0,
+                      rows=None, nthreads: int | None = None):
+        """The two steps in order: append each item's new K/V row at cache_lens[b], then
+        attend its query (at position cache_lens[b]) over the cache holding it.  Returns
+        (out, k_caches, v_caches).  Items without room have no keys: output 0."""
+        ko, vo = self.append(k_caches, v_caches, k_new, v_new, cache_lens)
+        cap = ko[0].shape[1] if ko else 0
+        cl = np.asarray(cache_lens, dtype=np.int64)
+        lens = np.where((cl >= 0) & (cl < cap), cl + 1, 0).astype(np.int32)
+        out = self.decode_per_cache(q, ko, vo, lens, scale=scale, window=window, rows=rows, nthreads=nthreads)
+        return out, ko, vo
+
     # ---- inspection --------------------------------------------------------------
     def prefill_probs(self, q, k, v, b: int, h: int, i: int, *, scale: float, causal: bool = False,
                       pos_offset: int = 0, seq_lens=None, window: int = 0):

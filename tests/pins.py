@@ -418,4 +418,96 @@ def pin_bf16_widening(oracle):
     _close(a, b, 0.0, "bf16 vs widened fp32")
 
 
+# ---------------------------------------------------------------------------
+# per-item caches and the fused append (ferrum-kernels `Backend`, Provided Methods:
+# `kv_cache_append_batched_per_cache`, `flash_attention_batched_per_cache`)
+
+def _per_item_caches(rng, B, Hkv, cap, D, dtype):
+    k = [draw(rng, (Hkv, cap, D), 1.0, dtype) for _ in range(B)]
+    v = [draw(rng, (Hkv, cap, D), 1.0, dtype) for _ in range(B)]
+    return k, v
+
+
+def pin_append_writes_one_slot(oracle):
+    """Only slot cache_lens[b] of every kv head of item b changes, to the new row; items
+    without room and the input caches are left as they were (checked slot by slot)."""
+    rng = _rng(500)
+    B, Hkv, cap, D = 4, 2, 6, 8
+    kc, vc = _per_item_caches(rng, B, Hkv, cap, D, "bf16")
+    kn = draw(rng, (B, Hkv, D), 1.0, "bf16")
+    vn = draw(rng, (B, Hkv, D), 1.0, "bf16")
+    keep_k, keep_v = [c.copy() for c in kc], [c.copy() for c in vc]
+    lens = np.array([0, 5, 6, -1], np.int32)   # first slot, last slot, full, negative
+    ko, vo = oracle.append(kc, vc, kn, vn, lens)
+    for b in range(B):
+        assert np.array_equal(kc[b], keep_k[b]) and np.array_equal(vc[b], keep_v[b]), "input cache modified"
+        for h in range(Hkv):
+            for j in range(cap):
+                written = j == lens[b] and 0 <= lens[b] < cap
+                want_k = kn[b, h] if written else keep_k[b][h, j]
+                want_v = vn[b, h] if written else keep_v[b][h, j]
+                assert np.array_equal(ko[b][h, j], want_k), f"K item {b} head {h} slot {j}"
+                assert np.array_equal(vo[b][h, j], want_v), f"V item {b} head {h} slot {j}"
+
+
+def pin_decode_append_brute_force(oracle):
+    """Append + decode == brute-force attention of the query at position L over the
+    explicitly concatenated keys [cache[:L], new] (causal, and the last-W window)."""
+    for n, (B, Hq, Hkv, cap, D, lens, W) in enumerate([
+            (3, 4, 2, 7, 8, [0, 3, 6], 0),
+            (3, 2, 1, 9, 4, [8, 2, 9], 3),
+            (2, 6, 3, 5, 8, [4, -2], 2)]):
+        rng = _rng(510 + n)
+        q = draw(rng, (B, Hq, D), 1.0, "f32")
+        kc, vc = _per_item_caches(rng, B, Hkv, cap, D, "f32")
+        kn = draw(rng, (B, Hkv, D), 1.0, "f32")
+        vn = draw(rng, (B, Hkv, D), 1.0, "f32")
+        scale = 0.45 + 0.1 * n
+        out, _, _ = oracle.decode_append(q, kn, vn, kc, vc, np.array(lens, np.int32), scale=scale, window=W)
+        for b in range(B):
+            L = lens[b]
+            if not 0 <= L < cap:
+                _close(out[b], np.zeros((Hq, D)), 0.0, f"case {n} item {b} without room")
+                continue
+            kf = np.concatenate([kc[b][:, :L], kn[b][:, None]], axis=1)[None]
+            vf = np.concatenate([vc[b][:, :L], vn[b][:, None]], axis=1)[None]
+            ref = brute.decode(q[b:b + 1], kf, vf, kv_len=L + 1, scale=scale, pos_offset=L, window=W)
+            _close(out[b], np.array(ref[0]), 1e-12, f"case {n} item {b}")
+
+
+def pin_decode_append_first_token(oracle):
+    """An empty cache (length 0): the new token is the only key, so the output is its V
+    row for every query head of the group, and a one-key window changes nothing."""
+    rng = _rng(520)
+    B, Hq, Hkv, cap, D = 2, 4, 2, 3, 8
+    q = draw(rng, (B, Hq, D), 1.0, "bf16")
+    kc, vc = _per_item_caches(rng, B, Hkv, cap, D, "bf16")
+    kn = draw(rng, (B, Hkv, D), 1.0, "bf16")
+    vn = draw(rng, (B, Hkv, D), 1.0, "bf16")
+    for W in (0, 1):
+        out, _, _ = oracle.decode_append(q, kn, vn, kc, vc, np.zeros(B, np.int32), scale=0.3, window=W)
+        for b in range(B):
+            for h in range(Hq):
+                _close(out[b, h], _f64(vn[b, h // 2]), 0.0, f"first token W={W} item {b} head {h}")
+
+
+def pin_decode_per_cache_equals_single_calls(oracle):
+    """One batched call over per-item caches == one single-item call per item on its own
+    cache (the loop the batched call replaces), and == brute force."""
+    rng = _rng(530)
+    B, Hq, Hkv, cap, D = 3, 4, 2, 10, 8
+    q = draw(rng, (B, Hq, D), 1.0, "f32")
+    kc, vc = _per_item_caches(rng, B, Hkv, cap, D, "f32")
+    lens = np.array([10, 1, 7], np.int32)
+    for W in (0, 3):
+        out = oracle.decode_per_cache(q, kc, vc, lens, scale=0.6, window=W)
+        for b in range(B):
+            one = oracle.decode(q[b:b + 1], kc[b][None], vc[b][None], kv_len=cap, scale=0.6, pos_offset=lens[b] - 1,
+                                window=W)
+            _close(out[b], one[0], 0.0, f"per-cache item {b} W={W}")
+            ref = brute.decode(q[b:b + 1], kc[b][None], vc[b][None], kv_len=cap, scale=0.6, kv_lens=lens[b:b + 1],
+                               window=W)
+            _close(out[b], np.array(ref[0]), 1e-12, f"per-cache brute item {b} W={W}")
+
+
 PINS = {name[4:]: fn for name, fn in sorted(globals().items()) if name.startswith("pin_") and callable(fn)}

@@ -5,6 +5,7 @@ a wrong sign, index or bound, a transposed or swapped operand), compiled on the 
 into a temporary library.  The real oracle is never modified.  A mutant that no pin
 rejects would mean the pins leave that part of the oracle unchecked.
 """
+import numpy as np
 import pytest
 
 import oracle
@@ -50,5 +51,72 @@ def test_mutant_is_caught(name, tmp_path):
         try:
             pin(m)
         except (AssertionError, ValueError):
+            caught.append(pin_name)
+    assert caught, f"no pin rejects the mutant {name}"
+
+
+# ---- the append and per-cache steps (numpy, in oracle/__init__.py) -----------------
+# Mutants of these are subclasses that override one step with a plausible mistake.
+
+class _AppendOneLate(oracle.Oracle):
+    @staticmethod
+    def append(k_caches, v_caches, k_new, v_new, cache_lens):
+        return oracle.Oracle.append(k_caches, v_caches, k_new, v_new, np.asarray(cache_lens) + 1)
+
+
+class _AppendKVSwapped(oracle.Oracle):
+    @staticmethod
+    def append(k_caches, v_caches, k_new, v_new, cache_lens):
+        return oracle.Oracle.append(k_caches, v_caches, v_new, k_new, cache_lens)
+
+
+class _AppendModifiesInput(oracle.Oracle):
+    @staticmethod
+    def append(k_caches, v_caches, k_new, v_new, cache_lens):
+        for b, n in enumerate(cache_lens):
+            if 0 <= n < k_caches[b].shape[1]:
+                k_caches[b][:, n, :] = k_new[b]
+                v_caches[b][:, n, :] = v_new[b]
+        return list(k_caches), list(v_caches)
+
+
+class _NewKeyNotAttended(oracle.Oracle):
+    def decode_append(self, q, k_new, v_new, k_caches, v_caches, cache_lens, *, scale, window=0, rows=None,
+                      nthreads=None):
+        ko, vo = self.append(k_caches, v_caches, k_new, v_new, cache_lens)
+        out = self.decode_per_cache(q, ko, vo, np.maximum(np.asarray(cache_lens, np.int32), 0), scale=scale,
+                                    window=window)
+        return out, ko, vo
+
+
+class _NoRoomAttendsAll(oracle.Oracle):
+    def decode_append(self, q, k_new, v_new, k_caches, v_caches, cache_lens, *, scale, window=0, rows=None,
+                      nthreads=None):
+        ko, vo = self.append(k_caches, v_caches, k_new, v_new, cache_lens)
+        cap = ko[0].shape[1]
+        cl = np.asarray(cache_lens, np.int64)
+        lens = np.where(cl < cap, cl + 1, cap).astype(np.int32)
+        return self.decode_per_cache(q, ko, vo, lens, scale=scale, window=window), ko, vo
+
+
+class _PerCacheItemsRotated(oracle.Oracle):
+    def decode_per_cache(self, q, k_caches, v_caches, kv_lens, *, scale, window=0, rows=None, nthreads=None):
+        k = list(k_caches[1:]) + list(k_caches[:1])
+        v = list(v_caches[1:]) + list(v_caches[:1])
+        return oracle.Oracle.decode_per_cache(self, q, k, v, kv_lens, scale=scale, window=window)
+
+
+PY_MUTANTS = {c.__name__[1:]: c for c in (_AppendOneLate, _AppendKVSwapped, _AppendModifiesInput,
+                                          _NewKeyNotAttended, _NoRoomAttendsAll, _PerCacheItemsRotated)}
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_python_step_mutant_is_caught(name):
+    m = PY_MUTANTS[name]()
+    caught = []
+    for pin_name, pin in PINS.items():
+        try:
+            pin(m)
+        except (AssertionError, ValueError, IndexError):
             caught.append(pin_name)
     assert caught, f"no pin rejects the mutant {name}"
