@@ -114,15 +114,24 @@ class Runner:
         lens = x.get("seq_lens") if w.kind == "prefill" else x.get("kv_lens")
         self.lens = None if lens is None else to_gpu(lens)
         self.ws = None
-        if w.kind == "decode":
+        if w.kind in ("decode", "decode_append"):
             n = mi.attn_decode_workspace_bytes(w.batch, w.q_heads, w.kv_heads, w.kv_len, w.head_dim)
             self.ws = torch.empty(max(n, 16), dtype=torch.uint8, device="cuda")
+        if w.kind == "decode_append":
+            self.k_new, self.v_new = to_gpu(x["k_new"]), to_gpu(x["v_new"])
+            self.lens = to_gpu(x["cache_lens"])
+            self.k_table, self.v_table = mi.CacheTable(self.k), mi.CacheTable(self.v)
 
     def __call__(self):
         w = self.w
         if w.kind == "prefill":
             self.mi.attn_prefill(self.q, self.k, self.v, self.out, pos_offset=w.pos_offset, seq_lens=self.lens,
                                  window=w.window, causal=w.causal, scale=w.attn_scale)
+        elif w.kind == "decode_append":
+            # the same slot is rewritten every step (the lengths are not advanced), so
+            # every step does the same work
+            self.mi.attn_decode_append(self.q, self.k_new, self.v_new, self.k_table, self.v_table, self.lens,
+                                       self.out, window=w.window, scale=w.attn_scale, workspace=self.ws)
         else:
             self.mi.attn_decode(self.q, self.k, self.v, self.out, kv_len=w.kv_len, pos_offset=w.pos_offset,
                                 kv_lens=self.lens, window=w.window, scale=w.attn_scale, workspace=self.ws)
@@ -187,8 +196,13 @@ def cpu_baseline_decode(w: W.Workload, x: dict, budget_s: float) -> dict:
     while True:
         pairs = pairs_all[:n].astype(np.int32)
         t0 = time.perf_counter()
-        ref.decode(x["q"], x["k"], x["v"], kv_len=w.kv_len, scale=w.attn_scale, pos_offset=w.pos_offset,
-                   window=w.window, rows=pairs, nthreads=nt)
+        if w.kind == "decode_append":
+            # the oracle's two steps: copy the caches with the new rows in, then attend
+            ref.decode_append(x["q"], x["k_new"], x["v_new"], list(x["k"]), list(x["v"]), x["cache_lens"],
+                              scale=w.attn_scale, window=w.window, rows=pairs, nthreads=nt)
+        else:
+            ref.decode(x["q"], x["k"], x["v"], kv_len=w.kv_len, scale=w.attn_scale, pos_offset=w.pos_offset,
+                       window=w.window, rows=pairs, nthreads=nt)
         dt = time.perf_counter() - t0
         if dt >= budget_s / 4 or n == total:
             break

@@ -10,11 +10,16 @@ missing library or GPU raises.
                  causal=False, scale=None)
     attn_decode(q, k_cache, v_cache, out=None, *, kv_len=None, pos_offset=None,
                 kv_lens=None, window=0, scale=None, workspace=None)
+    attn_decode_per_cache(q, k_caches, v_caches, kv_lens, out=None, *, window=0,
+                          scale=None, workspace=None)
+    attn_decode_append(q, k_new, v_new, k_caches, v_caches, cache_lens, out=None, *,
+                       window=0, scale=None, workspace=None)
     attn_decode_workspace_bytes(batch, q_heads, kv_heads, kv_len, head_dim)
     attn_last_error(), attn_version()
 
 Layouts: q [batch, q_heads, q_len, head_dim]; k, v [batch, kv_heads, kv_len, head_dim];
-decode caches [batch, kv_heads, capacity, head_dim] (head-major).  scale defaults to
+decode caches [batch, kv_heads, capacity, head_dim] (head-major); the per-cache calls
+take one [kv_heads, capacity, head_dim] cache per item.  scale defaults to
 1/sqrt(head_dim).
 """
 from __future__ import annotations
@@ -28,7 +33,8 @@ LIBRARY = Path(__file__).resolve().parent / "libmi_attn.so"
 MI_ATTN_F32, MI_ATTN_BF16 = 0, 1
 MI_ATTN_OK, MI_ATTN_ERR_INVALID, MI_ATTN_ERR_UNSUPPORTED, MI_ATTN_ERR_HIP = 0, 1, 2, 3
 
-EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_workspace_bytes", "attn_last_error", "attn_version")
+EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_per_cache", "attn_decode_append",
+           "attn_decode_workspace_bytes", "attn_last_error", "attn_version")
 
 
 class MiAttnError(RuntimeError):
@@ -52,6 +58,10 @@ def library() -> ctypes.CDLL:
         lib.attn_prefill.restype = i
         lib.attn_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, i, f, i, vp, sz, vp]
         lib.attn_decode.restype = i
+        lib.attn_decode_per_cache.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, i, f, i, vp, sz, vp]
+        lib.attn_decode_per_cache.restype = i
+        lib.attn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, i, f, i, vp, sz, vp]
+        lib.attn_decode_append.restype = i
         lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
         lib.attn_decode_workspace_bytes.restype = sz
         lib.attn_last_error.argtypes = []
@@ -173,5 +183,129 @@ def attn_decode(q, k_cache, v_cache, out=None, *, kv_len: int | None = None, pos
     st = library().attn_decode(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(out, "out"),
                                B, Hq, Hkv, kv_len, cap, D, pos_offset, _dev(kv_lens, "kv_lens"), window,
                                float(scale), dt, _dev(workspace, "workspace"), ws_bytes, _stream(stream))
+    _check(st)
+    return out
+
+
+class CacheTable:
+    """The device array of per-item cache pointers the per-cache calls take, built once.
+
+    Passing one of these instead of a list of tensors saves the host-to-device copy of
+    the pointer array on every call (a decode loop builds it once per set of caches).
+    It keeps the cache tensors alive."""
+
+    def __init__(self, caches, batch: int | None = None, name: str = "caches"):
+        if isinstance(caches, (list, tuple)):
+            first = caches[0]
+            B = len(caches)
+        else:
+            first, B = caches, caches.shape[0]
+        if batch is not None and B != batch:
+            raise ValueError(f"{name}: {B} caches for batch {batch}")
+        self.ptrs, self.dims = _cache_pointers(caches, B, name, first.dtype, first.device)
+        self.batch, self.dtype, self.caches = B, first.dtype, caches
+
+
+def _cache_pointers(caches, B: int, name: str, dtype, device):
+    """Device int64 tensor of `B` cache base pointers, and (kv_heads, capacity, head_dim).
+
+    `caches` is a list of `B` contiguous tensors [kv_heads, capacity, head_dim] (one per
+    item, any allocation), one contiguous [B, kv_heads, capacity, head_dim] tensor (its
+    items' bases are used), or a CacheTable."""
+    torch = _torch()
+    if isinstance(caches, CacheTable):
+        if caches.batch != B or caches.dtype != dtype:
+            raise ValueError(f"{name}: cache table of batch {caches.batch}, {caches.dtype} for batch {B}, {dtype}")
+        return caches.ptrs, caches.dims
+    if isinstance(caches, (list, tuple)):
+        if len(caches) != B:
+            raise ValueError(f"{name}: {len(caches)} caches for batch {B}")
+        shapes = {tuple(c.shape) for c in caches}
+        if len(shapes) != 1 or len(next(iter(shapes))) != 3:
+            raise ValueError(f"{name}: every cache must be [kv_heads, capacity, head_dim] of one shape")
+        for c in caches:
+            _dev(c, name, dtype)
+            if c.data_ptr() % 16:
+                raise ValueError(f"{name}: caches must be 16-byte aligned")
+        ptrs = [c.data_ptr() for c in caches]
+        dims = next(iter(shapes))
+    else:
+        if caches.dim() != 4 or caches.shape[0] != B:
+            raise ValueError(f"{name}: expected [B, kv_heads, capacity, head_dim] or a list of caches")
+        _dev(caches, name, dtype)
+        step = caches.stride(0) * caches.element_size()
+        ptrs = [caches.data_ptr() + b * step for b in range(B)]
+        dims = tuple(caches.shape[1:])
+    return torch.tensor(ptrs, dtype=torch.int64, device=device), dims
+
+
+def _keep_for(stream, *tensors) -> None:
+    """The pointer arrays are freed when the call returns; torch's allocator orders their
+    reuse on the current stream, so only a call on another torch stream needs this."""
+    if stream is not None and hasattr(stream, "cuda_stream"):
+        for t in tensors:
+            t.record_stream(stream)
+
+
+def _decode_common(q, k_caches, v_caches, lens, out, workspace, what: str):
+    torch = _torch()
+    if q.dim() != 3:
+        raise ValueError("q must be [B,Hq,D]")
+    B, Hq, D = q.shape
+    kp, kd = _cache_pointers(k_caches, B, "k_caches", q.dtype, q.device)
+    vp, vd = _cache_pointers(v_caches, B, "v_caches", q.dtype, q.device)
+    if kd != vd:
+        raise ValueError("K and V caches differ in shape")
+    Hkv, cap, Dk = kd
+    if Dk != D:
+        raise ValueError("q and the caches disagree on head_dim")
+    if lens is None or lens.dtype != torch.int32 or lens.numel() != B:
+        raise ValueError(f"{what} must be an int32 tensor of batch elements")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    need = attn_decode_workspace_bytes(B, Hq, Hkv, cap, D) if Hq % Hkv == 0 else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return B, Hq, Hkv, cap, D, kp, vp, out, workspace, ws_bytes
+
+
+def attn_decode_per_cache(q, k_caches, v_caches, kv_lens, out=None, *, window: int = 0,
+                          scale: float | None = None, workspace=None, stream=None):
+    """Decode over one cache per item (a list of [kv_heads, capacity, head_dim] tensors);
+    returns `out` [batch, q_heads, head_dim]."""
+    dt = _dtype_code(q)
+    B, Hq, Hkv, cap, D, kp, vp, out, workspace, ws_bytes = _decode_common(q, k_caches, v_caches, kv_lens, out,
+                                                                          workspace, "kv_lens")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = library().attn_decode_per_cache(_dev(q, "q"), _dev(kp, "k_caches"), _dev(vp, "v_caches"), _dev(out, "out"),
+                                         B, Hq, Hkv, cap, D, _dev(kv_lens, "kv_lens"), window, float(scale), dt,
+                                         _dev(workspace, "workspace"), ws_bytes, _stream(stream))
+    _keep_for(stream, kp, vp)
+    _check(st)
+    return out
+
+
+def attn_decode_append(q, k_new, v_new, k_caches, v_caches, cache_lens, out=None, *, window: int = 0,
+                       scale: float | None = None, workspace=None, stream=None):
+    """Append the new token's K/V rows [batch, kv_heads, head_dim] at slot cache_lens[b] of
+    each item's caches, then decode its query over them; returns `out`.  The caches are
+    modified in place; cache_lens is not (the caller advances it)."""
+    dt = _dtype_code(q)
+    B, Hq, Hkv, cap, D, kp, vp, out, workspace, ws_bytes = _decode_common(q, k_caches, v_caches, cache_lens, out,
+                                                                          workspace, "cache_lens")
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        if tuple(t.shape) != (B, Hkv, D) or t.dtype != q.dtype:
+            raise ValueError(f"{nm} must be [batch, kv_heads, head_dim] of q's dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = library().attn_decode_append(_dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                                      _dev(kp, "k_caches"), _dev(vp, "v_caches"), _dev(out, "out"), B, Hq, Hkv,
+                                      cap, D, _dev(cache_lens, "cache_lens"), window, float(scale), dt,
+                                      _dev(workspace, "workspace"), ws_bytes, _stream(stream))
+    _keep_for(stream, kp, vp)
     _check(st)
     return out

@@ -161,3 +161,96 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o
 }
 
 }  // extern "C"
+
+namespace {
+
+// Shared checks and launch of the per-item-cache decode calls.
+int decode_per_item(const char* fn, const void* q, const void* const* k_caches, const void* const* v_caches,
+                    const void* k_new, const void* v_new, void* out, int batch, int q_heads, int kv_heads,
+                    int capacity, int head_dim, const int32_t* lens, int window, float scale, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    g_error[0] = '\0';
+    if (dtype != MI_ATTN_BF16 && dtype != MI_ATTN_F32)
+        return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+    if (batch < 0) return fail(MI_ATTN_ERR_INVALID, "%s: negative batch (%d)", fn, batch);
+    if (q_heads < 1 || kv_heads < 1)
+        return fail(MI_ATTN_ERR_INVALID, "%s: q_heads (%d) and kv_heads (%d) must be >= 1", fn, q_heads,
+                    kv_heads);
+    if (q_heads % kv_heads != 0)
+        return fail(MI_ATTN_ERR_INVALID, "%s: q_heads (%d) is not a multiple of kv_heads (%d)", fn, q_heads,
+                    kv_heads);
+    if (capacity < 1) return fail(MI_ATTN_ERR_INVALID, "%s: capacity (%d) must be >= 1", fn, capacity);
+    if (window < 0) return fail(MI_ATTN_ERR_INVALID, "%s: window (%d) is negative", fn, window);
+    if (!std::isfinite(scale)) return fail(MI_ATTN_ERR_INVALID, "%s: scale is not finite", fn);
+    if (!supported_head_dim(head_dim))
+        return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: head_dim %d is not one of 32, 64, 128", fn, head_dim);
+    if (batch == 0) return MI_ATTN_OK;
+    if (!q || !k_caches || !v_caches || !out || !lens)
+        return fail(MI_ATTN_ERR_INVALID, "%s: null pointer argument", fn);
+    if (k_new && (!v_new || !aligned16(k_new) || !aligned16(v_new)))
+        return fail(MI_ATTN_ERR_INVALID, "%s: new K/V rows must both be given, 16-byte aligned", fn);
+    if (!aligned16(q) || !aligned16(out))
+        return fail(MI_ATTN_ERR_INVALID, "%s: tensors must be 16-byte aligned", fn);
+    if (((uintptr_t)k_caches & 7u) || ((uintptr_t)v_caches & 7u) || ((uintptr_t)lens & 3u))
+        return fail(MI_ATTN_ERR_INVALID, "%s: pointer arrays must be 8-byte and lengths 4-byte aligned", fn);
+    if ((long)batch > 65535 || (long)q_heads > 65535)
+        return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: q_heads and batch must be <= 65535", fn);
+    const size_t need = attn_decode_workspace_bytes(batch, q_heads, kv_heads, capacity, head_dim);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(MI_ATTN_ERR_INVALID, "%s: workspace of %zu bytes given, %zu needed", fn, workspace_bytes,
+                    need);
+    if (!aligned16(workspace)) return fail(MI_ATTN_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
+
+    const mi_attn::DecodePlan p = mi_attn::plan_decode(batch, q_heads, kv_heads, capacity, head_dim);
+    mi_attn::DecodeArgs a{};
+    a.q = q;
+    a.k_ptrs = k_caches;
+    a.v_ptrs = v_caches;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.out = out;
+    a.ws = (float*)workspace;
+    a.kv_lens = lens;
+    a.batch = batch;
+    a.q_heads = q_heads;
+    a.kv_heads = kv_heads;
+    a.kv_len = capacity;
+    a.capacity = capacity;
+    a.window = window;
+    a.scale = scale;
+    a.splits = p.splits;
+    a.split_len = p.split_len;
+    a.head_groups = p.head_groups;
+    hipError_t e = mi_attn::launch_decode(a, head_dim, p.heads_per_group, dtype == MI_ATTN_BF16,
+                                          (hipStream_t)stream);
+    if (e != hipSuccess) return fail(MI_ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return MI_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_per_cache(const void* q, const void* const* k_caches, const void* const* v_caches, void* out,
+                          int batch, int q_heads, int kv_heads, int capacity, int head_dim,
+                          const int32_t* kv_lens, int window, float scale, int dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    return decode_per_item("attn_decode_per_cache", q, k_caches, v_caches, nullptr, nullptr, out, batch, q_heads,
+                           kv_heads, capacity, head_dim, kv_lens, window, scale, dtype, workspace,
+                           workspace_bytes, stream);
+}
+
+int attn_decode_append(const void* q, const void* k_new, const void* v_new, void* const* k_caches,
+                       void* const* v_caches, void* out, int batch, int q_heads, int kv_heads, int capacity,
+                       int head_dim, const int32_t* cache_lens, int window, float scale, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    if (batch > 0 && (!k_new || !v_new)) {
+        g_error[0] = '\0';
+        return fail(MI_ATTN_ERR_INVALID, "attn_decode_append: null new K/V rows");
+    }
+    return decode_per_item("attn_decode_append", q, (const void* const*)k_caches, (const void* const*)v_caches,
+                           k_new, v_new, out, batch, q_heads, kv_heads, capacity, head_dim, cache_lens, window,
+                           scale, dtype, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

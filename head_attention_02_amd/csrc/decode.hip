@@ -55,7 +55,24 @@ __device__ __forceinline__ void load8(const void* base, size_t elem, float* x) {
     }
 }
 
-template <int D, int GT, bool BF16>
+// The 16 (bf16) or 32 (fp32) bytes of eight consecutive elements, copied unchanged.
+template <bool BF16>
+__device__ __forceinline__ void copy8(const void* src, size_t src_elem, void* dst, size_t dst_elem) {
+    constexpr int esz = BF16 ? 2 : 4;
+    const u32x4* s = (const u32x4*)((const char*)src + src_elem * esz);
+    u32x4* d = (u32x4*)((char*)dst + dst_elem * esz);
+    d[0] = s[0];
+    if constexpr (!BF16) d[1] = s[1];
+}
+
+// Cache addressing modes of the split kernel.
+enum CacheMode {
+    kStacked = 0,   // caches [batch, kv_heads, capacity, D] in one allocation
+    kPerItem = 1,   // one [kv_heads, capacity, D] allocation per item, via a pointer array
+    kAppend = 2,    // per item, and the new token's K/V row is appended before attending
+};
+
+template <int D, int GT, bool BF16, int MODE>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     constexpr int LPR = D / 8;            // lanes per key row, 8 elements per lane
     constexpr int RPW = 64 / LPR;         // rows per wave load
@@ -79,7 +96,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 
     // query position and the key interval [lo, hi] it sees
     int len, pos;
-    if (a.kv_lens) {
+    if constexpr (MODE == kAppend) {
+        // kv_lens holds the lengths before the append: the new token goes to slot
+        // kv_lens[b] and its query sits there.  No room (a length outside
+        // [0, capacity)): nothing is written and the output is zero.
+        const int cl = a.kv_lens[b];
+        len = (cl >= 0 && cl < a.capacity) ? cl + 1 : 0;
+        pos = len - 1;
+    } else if (a.kv_lens) {
         len = min(max(a.kv_lens[b], 0), a.kv_len);
         pos = len - 1;
     } else {
@@ -110,7 +134,25 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         for (int i = 0; i < 8; ++i) o[t][i] = 0.0f;
     }
 
-    const size_t head_base = ((size_t)b * a.kv_heads + kvh) * (size_t)a.capacity * D;
+    const void* kc = a.k;
+    const void* vc = a.v;
+    size_t head_base = ((size_t)b * a.kv_heads + kvh) * (size_t)a.capacity * D;
+    if constexpr (MODE != kStacked) {
+        kc = a.k_ptrs[b];
+        vc = a.v_ptrs[b];
+        head_base = (size_t)kvh * a.capacity * D;
+    }
+    // append: the row at the query position comes from the new token (registers of the
+    // lanes that read it), not from the cache; the split that holds the position also
+    // stores the new rows into the cache (first head group only).  No other workgroup
+    // reads that slot, so the store does not race with the reads.
+    const size_t new_row = ((size_t)b * a.kv_heads + kvh) * D + c * 8;
+    if constexpr (MODE == kAppend) {
+        if (hg == 0 && pos >= s0 && pos < s1 && tid < LPR) {
+            copy8<BF16>(a.k_new, new_row, (void*)kc, head_base + (size_t)pos * D + c * 8);
+            copy8<BF16>(a.v_new, new_row, (void*)vc, head_base + (size_t)pos * D + c * 8);
+        }
+    }
     for (int base = s0; base < s1; base += BATCH) {
         int key[kSteps];
         float kx[kSteps][8];
@@ -118,7 +160,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         for (int u = 0; u < kSteps; ++u) {
             key[u] = base + (u * kWaves + wave) * RPW + r;
             const int kr = key[u] < s1 ? key[u] : s0;     // out-of-range rows read a valid row
-            load8<BF16, true>(a.k, head_base + (size_t)kr * D + c * 8, kx[u]);
+            if constexpr (MODE == kAppend) {
+                const bool nw = kr == pos;
+                load8<BF16, true>(nw ? a.k_new : kc, nw ? new_row : head_base + (size_t)kr * D + c * 8, kx[u]);
+            } else {
+                load8<BF16, true>(kc, head_base + (size_t)kr * D + c * 8, kx[u]);
+            }
         }
         float s[kSteps][GT];
 #pragma unroll
@@ -136,7 +183,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int u = 0; u < kSteps; ++u) {
             const int kr = key[u] < s1 ? key[u] : s0;
-            load8<BF16, true>(a.v, head_base + (size_t)kr * D + c * 8, vx[u]);
+            if constexpr (MODE == kAppend) {
+                const bool nw = kr == pos;
+                load8<BF16, true>(nw ? a.v_new : vc, nw ? new_row : head_base + (size_t)kr * D + c * 8, vx[u]);
+            } else {
+                load8<BF16, true>(vc, head_base + (size_t)kr * D + c * 8, vx[u]);
+            }
         }
 #pragma unroll
         for (int t = 0; t < GT; ++t) {
@@ -228,16 +280,27 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
     }
 }
 
+template <int D, bool BF16, int MODE>
+void launch_split(const DecodeArgs& a, int gt, dim3 grid, hipStream_t stream) {
+    const dim3 block(kThreads);
+    switch (gt) {
+        case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1, BF16, MODE>), grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, BF16, MODE>), grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((decode_split_kernel<D, 4, BF16, MODE>), grid, block, 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((decode_split_kernel<D, 8, BF16, MODE>), grid, block, 0, stream, a); break;
+    }
+}
+
 template <int D, bool BF16>
 hipError_t launch_d(const DecodeArgs& a, int gt, hipStream_t stream) {
-    dim3 grid(a.splits, a.kv_heads * a.head_groups, a.batch), block(kThreads);
-    switch (gt) {
-        case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1, BF16>), grid, block, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, BF16>), grid, block, 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((decode_split_kernel<D, 4, BF16>), grid, block, 0, stream, a); break;
-        case 8: hipLaunchKernelGGL((decode_split_kernel<D, 8, BF16>), grid, block, 0, stream, a); break;
-        default: return hipErrorInvalidValue;
-    }
+    if (gt != 1 && gt != 2 && gt != 4 && gt != 8) return hipErrorInvalidValue;
+    const dim3 grid(a.splits, a.kv_heads * a.head_groups, a.batch);
+    if (a.k_new)
+        launch_split<D, BF16, kAppend>(a, gt, grid, stream);
+    else if (a.k_ptrs)
+        launch_split<D, BF16, kPerItem>(a, gt, grid, stream);
+    else
+        launch_split<D, BF16, kStacked>(a, gt, grid, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
     hipLaunchKernelGGL((decode_combine_kernel<D, BF16>), dim3(a.batch * a.q_heads), dim3(D), 0, stream, a);

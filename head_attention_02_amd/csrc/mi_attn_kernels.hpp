@@ -33,6 +33,15 @@ struct DecodeArgs {
     float scale;
     int splits, split_len;    // key-range split of each (item, kv head)
     int head_groups;          // query-head groups per kv head (grid.y = kv_heads * head_groups)
+    // Per-item caches (attn_decode_per_cache, attn_decode_append): device arrays of
+    // `batch` pointers, each to one item's [kv_heads, capacity, head_dim] cache; k and v
+    // are then unused.  nullptr: the stacked caches k, v.
+    const void* const* k_ptrs;
+    const void* const* v_ptrs;
+    // attn_decode_append: the new token's rows [batch, kv_heads, head_dim]; kv_lens then
+    // holds the cache lengths before the append.  nullptr: no append.
+    const void* k_new;
+    const void* v_new;
 };
 
 // Each launcher enqueues on `stream` and returns the launch status.

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_VERSION 1
+#define MI_ATTN_VERSION 2
 
 typedef enum { MI_ATTN_F32 = 0, MI_ATTN_BF16 = 1 } mi_attn_dtype;
 
@@ -119,8 +119,64 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o
                 const int32_t* kv_lens, int window, float scale, int dtype, void* workspace,
                 size_t workspace_bytes, void* stream);
 
+/*
+ * attn_decode_per_cache -- attn_decode over one separately allocated cache per item.
+ * Follows `flash_attention_batched_per_cache` of the ferrum-kernels `Backend` page
+ * (Provided Methods): M decode caches, each [kv_heads, capacity, head_dim] head-major,
+ * attended in one launch, with per-item lengths in a device buffer and a common
+ * sliding window.
+ *
+ *   q         [batch, q_heads, head_dim]
+ *   k_caches  DEVICE array of `batch` DEVICE pointers (8-byte aligned array); entry b
+ *             points at item b's K cache [kv_heads, capacity, head_dim], 16-byte aligned
+ *   v_caches  the same for V
+ *   out       [batch, q_heads, head_dim]
+ *   kv_lens   DEVICE int32 [batch], required: item b has kv_lens[b] keys (clamped to
+ *             [0, capacity]) in slots [0, kv_lens[b]) and its query sits at
+ *             kv_lens[b] - 1; an item with no keys gets zeros.
+ *   window    0: all causal keys; w > 0: only the last w positions.
+ *   workspace as for attn_decode, sized attn_decode_workspace_bytes(batch, q_heads,
+ *             kv_heads, capacity, head_dim).
+ *   The pointed-to caches are read only.  The pointer arrays, the caches and kv_lens
+ *   are device memory the host does not inspect: a wrong pointer in them faults on the
+ *   device, it is not reported by the call.
+ */
+int attn_decode_per_cache(const void* q, const void* const* k_caches, const void* const* v_caches, void* out,
+                          int batch, int q_heads, int kv_heads, int capacity, int head_dim,
+                          const int32_t* kv_lens, int window, float scale, int dtype, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_append -- append the new token's K and V rows to each item's cache, then
+ * attend its query over the cache including them, in one launch.  Fuses
+ * `kv_cache_append_batched_per_cache` (each item's head-major row goes into its own
+ * cache at the offset read from cache_lens[i]) with `flash_attention_batched_per_cache`
+ * of the ferrum-kernels `Backend` page; `split_qkv_norm_rope_into_cache` on the same
+ * page is the same idea of dropping the separate append dispatch.
+ *
+ *   q           [batch, q_heads, head_dim]  the new token's queries
+ *   k_new, v_new [batch, kv_heads, head_dim] the new token's keys and values
+ *   k_caches, v_caches  DEVICE arrays of `batch` DEVICE pointers to item caches
+ *               [kv_heads, capacity, head_dim]; slot cache_lens[b] of every kv head of
+ *               item b is overwritten with the new row, nothing else is written.
+ *   cache_lens  DEVICE int32 [batch], required: the number of tokens already in each
+ *               cache (the caller owns this bookkeeping and advances it after the call).
+ *               Item b's query sits at position cache_lens[b] and sees the keys
+ *               [0, cache_lens[b]] (the new one included), or the last `window` of them.
+ *               An item with no room (cache_lens[b] < 0 or >= capacity) is left
+ *               untouched and gets zeros.
+ *   out, window, scale, dtype, workspace as for attn_decode_per_cache.
+ *   Two items must not share a cache.  The caller must not read or write the caches
+ *   until the call's kernels finish.
+ */
+int attn_decode_append(const void* q, const void* k_new, const void* v_new, void* const* k_caches,
+                       void* const* v_caches, void* out, int batch, int q_heads, int kv_heads, int capacity,
+                       int head_dim, const int32_t* cache_lens, int window, float scale, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Scratch bytes attn_decode needs for these sizes (0 when it needs none).  Pure host
- * function; returns 0 for sizes attn_decode would reject. */
+ * function; returns 0 for sizes attn_decode would reject.  For attn_decode_per_cache and
+ * attn_decode_append pass capacity as kv_len. */
 size_t attn_decode_workspace_bytes(int batch, int q_heads, int kv_heads, int kv_len, int head_dim);
 
 /* Message of the calling thread's last failed call ("" if none).  The pointer stays

@@ -113,3 +113,59 @@ def test_error_message_is_cleared_by_a_good_call():
     assert mi.attn_last_error()
     assert prefill(batch=0) == mi.MI_ATTN_OK
     assert mi.attn_last_error() == ""
+
+
+def per_cache(**kw):
+    args = dict(q=FAKE, kc=FAKE, vc=FAKE, out=FAKE, batch=2, q_heads=8, kv_heads=2, capacity=16, head_dim=64,
+                kv_lens=FAKE, window=0, scale=0.125, dtype=mi.MI_ATTN_BF16, ws=FAKE, ws_bytes=1 << 30,
+                stream=None)
+    args.update(kw)
+    return mi.library().attn_decode_per_cache(*args.values())
+
+
+def append(**kw):
+    args = dict(q=FAKE, k_new=FAKE, v_new=FAKE, kc=FAKE, vc=FAKE, out=FAKE, batch=2, q_heads=8, kv_heads=2,
+                capacity=16, head_dim=64, cache_lens=FAKE, window=0, scale=0.125, dtype=mi.MI_ATTN_BF16, ws=FAKE,
+                ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return mi.library().attn_decode_append(*args.values())
+
+
+COMMON_PER_ITEM_ERRORS = [
+    (dict(q_heads=6, kv_heads=4), mi.MI_ATTN_ERR_INVALID, "not a multiple"),
+    (dict(capacity=0), mi.MI_ATTN_ERR_INVALID, "capacity"),
+    (dict(window=-1), mi.MI_ATTN_ERR_INVALID, "negative"),
+    (dict(scale=math.nan), mi.MI_ATTN_ERR_INVALID, "not finite"),
+    (dict(head_dim=80), mi.MI_ATTN_ERR_UNSUPPORTED, "head_dim 80"),
+    (dict(dtype=5), mi.MI_ATTN_ERR_UNSUPPORTED, "dtype"),
+    (dict(kc=None), mi.MI_ATTN_ERR_INVALID, "null"),
+    (dict(out=ctypes.c_void_p(0x100008)), mi.MI_ATTN_ERR_INVALID, "aligned"),
+    (dict(vc=ctypes.c_void_p(0x100004)), mi.MI_ATTN_ERR_INVALID, "aligned"),
+    # 4096 slots of 4 (item, kv head) units are split, so a workspace is needed
+    (dict(capacity=4096, ws_bytes=16), mi.MI_ATTN_ERR_INVALID, "workspace"),
+]
+
+
+@pytest.mark.parametrize("kw,status,msg", COMMON_PER_ITEM_ERRORS + [
+    (dict(kv_lens=None), mi.MI_ATTN_ERR_INVALID, "null"),
+])
+def test_decode_per_cache_validation(kw, status, msg):
+    assert per_cache(**kw) == status
+    err = mi.attn_last_error()
+    assert err.startswith("attn_decode_per_cache: ") and msg in err
+
+
+@pytest.mark.parametrize("kw,status,msg", COMMON_PER_ITEM_ERRORS + [
+    (dict(cache_lens=None), mi.MI_ATTN_ERR_INVALID, "null"),
+    (dict(k_new=None), mi.MI_ATTN_ERR_INVALID, "new K/V"),
+    (dict(v_new=ctypes.c_void_p(0x100002)), mi.MI_ATTN_ERR_INVALID, "new K/V"),
+])
+def test_decode_append_validation(kw, status, msg):
+    assert append(**kw) == status
+    err = mi.attn_last_error()
+    assert err.startswith("attn_decode_append: ") and msg in err
+
+
+def test_per_item_empty_batch_is_ok_without_a_gpu():
+    assert per_cache(batch=0, kv_lens=None) == mi.MI_ATTN_OK
+    assert append(batch=0, k_new=None, v_new=None) == mi.MI_ATTN_OK

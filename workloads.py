@@ -12,6 +12,7 @@ bits.  Padded positions keep their random values.
 The five named workloads are the shapes the pages' backends run attention on: a tiny
 fp32 causal check, a BERT-base encoder batch with padding, a ModernBERT-style local
 (banded) layer, a causal GQA prefill and a batched GQA decode over a head-major cache.
+A sixth is that decode with the new token's K/V row appended to the cache first.
 """
 from __future__ import annotations
 
@@ -51,7 +52,7 @@ def draw(rng: np.random.Generator, shape, sigma: float, dtype: str) -> np.ndarra
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "prefill" or "decode"
+    kind: str                 # "prefill", "decode" or "decode_append"
     batch: int
     q_heads: int
     kv_heads: int
@@ -84,6 +85,10 @@ WORKLOADS = {
                                  True, scale=1.0 / math.sqrt(128), seed=4),
     "gqa_decode_kv8192": Workload("gqa_decode_kv8192", "decode", 64, 32, 8, 1, 8192, 128, "bf16", 1.0,
                                   True, pos_offset=8191, capacity=8192, seed=5),
+    # the same decode step with the new token's K/V row appended to each item's cache
+    # first: 8191 tokens already cached, the new one goes to slot 8191
+    "gqa_decode_append_kv8192": Workload("gqa_decode_append_kv8192", "decode_append", 64, 32, 8, 1, 8192, 128,
+                                         "bf16", 1.0, True, pos_offset=8191, capacity=8192, seed=6),
 }
 
 
@@ -92,6 +97,9 @@ def make_inputs(w: Workload) -> dict:
 
     prefill: q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D], seq_lens [B] int32 or None
     decode:  q [B,Hq,D], k/v caches [B,Hkv,capacity,D], kv_lens None
+    decode_append: as decode, then the new rows k_new/v_new [B,Hkv,D] (drawn after the
+             caches) and cache_lens [B] int32 (the per-item lengths when drawn, else
+             pos_offset for every item)
     """
     rng = np.random.default_rng(w.seed)
     seq_lens = None
@@ -107,6 +115,11 @@ def make_inputs(w: Workload) -> dict:
     q = draw(rng, (w.batch, w.q_heads, w.head_dim), w.sigma, w.dtype)
     k = draw(rng, (w.batch, w.kv_heads, cap, w.head_dim), w.sigma, w.dtype)
     v = draw(rng, (w.batch, w.kv_heads, cap, w.head_dim), w.sigma, w.dtype)
+    if w.kind == "decode_append":
+        k_new = draw(rng, (w.batch, w.kv_heads, w.head_dim), w.sigma, w.dtype)
+        v_new = draw(rng, (w.batch, w.kv_heads, w.head_dim), w.sigma, w.dtype)
+        cache_lens = seq_lens if seq_lens is not None else np.full(w.batch, w.pos_offset, np.int32)
+        return {"q": q, "k": k, "v": v, "k_new": k_new, "v_new": v_new, "cache_lens": cache_lens}
     return {"q": q, "k": k, "v": v, "kv_lens": seq_lens}
 
 
