@@ -14,7 +14,8 @@ the stream the kernels run on.  `--workload` benchmarks one other named workload
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 `--workload copy_calibration` runs a plain 1 GiB device copy instead, the known-size
-reference against which the rocprofv3 FETCH_SIZE / WRITE_SIZE counters are scaled.
+reference against which the rocprofv3 FETCH_SIZE / WRITE_SIZE counters are scaled;
+`--record-traffic DIR` (no GPU) turns those counter runs into profiles/traffic.json.
 """
 from __future__ import annotations
 
@@ -245,6 +246,62 @@ def copy_calibration(steps: int, warmup: int) -> int:
 
 
 # ---------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counter runs -> profiles/traffic.json
+
+# (run label, workload, kernel-name prefixes that make up one call, kernel sources)
+TRAFFIC_RUNS = [
+    ("head", "causal_gqa_s4096", ["prefill_bf16_kernel<128"], ["prefill_bf16.hip", "mi_attn_device.hpp"]),
+    ("head", "gqa_decode_kv8192", ["decode_split_kernel<128", "decode_combine_kernel<128"],
+     ["decode.hip", "mi_attn_device.hpp"]),
+    ("append", "gqa_decode_append_kv8192", ["decode_split_kernel<128", "decode_combine_kernel<128"],
+     ["decode.hip", "mi_attn_device.hpp"]),
+]
+
+
+def _counter_rows(run_dir: Path, counter: str):
+    """(kernel name, value) per dispatch from a rocprofv3 --pmc csv run."""
+    import csv
+    files = sorted(run_dir.rglob("*counter_collection.csv"))
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def _per_dispatch(rows, prefix: str) -> float:
+    vals = [v for name, v in rows if prefix in name]
+    return float(np.mean(vals)) if vals else 0.0
+
+
+def record_traffic(run_root: Path) -> dict:
+    """Reads <run_root>/{head,append,copy}_{FETCH_SIZE,WRITE_SIZE} (one rocprofv3 --pmc run
+    each) and writes profiles/traffic.json: HBM bytes per call of each workload, with the
+    counters scaled by what they read for the 1 GiB copy."""
+    cf = _per_dispatch(_counter_rows(run_root / "copy_FETCH_SIZE", "FETCH_SIZE"), "copyBuffer")
+    cw = _per_dispatch(_counter_rows(run_root / "copy_WRITE_SIZE", "WRITE_SIZE"), "copyBuffer")
+    ff, wf = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
+    out = {"_calibration": {"kernel": "__amd_rocclr_copyBuffer", "bytes_read": COPY_BYTES,
+                            "bytes_written": COPY_BYTES, "FETCH_SIZE_KiB": cf, "WRITE_SIZE_KiB": cw,
+                            "fetch_factor": ff, "write_factor": wf}}
+    for label, name, prefixes, src in TRAFFIC_RUNS:
+        fr = _counter_rows(run_root / f"{label}_FETCH_SIZE", "FETCH_SIZE")
+        wr = _counter_rows(run_root / f"{label}_WRITE_SIZE", "WRITE_SIZE")
+        fk = sum(_per_dispatch(fr, p) for p in prefixes)
+        wk = sum(_per_dispatch(wr, p) for p in prefixes)
+        rd, wt = fk * 1024 * ff, wk * 1024 * wf
+        out[name] = {"source_digest": kernel_sources_digest(src), "kernels": prefixes,
+                     "FETCH_SIZE_KiB": fk, "WRITE_SIZE_KiB": wk, "bytes_read": rd, "bytes_written": wt,
+                     "bytes_per_launch": rd + wt}
+    (PROFILES / "traffic.json").write_text(json.dumps(out, indent=1) + "\n")
+    return out
+
+
+# ---------------------------------------------------------------------------
 
 
 def main() -> int:
@@ -257,7 +314,13 @@ def main() -> int:
                          "workloads.WORKLOADS, or copy_calibration (1 GiB device copy for the HBM counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work per baseline")
+    ap.add_argument("--record-traffic", metavar="DIR",
+                    help="no GPU run: turn the rocprofv3 FETCH_SIZE / WRITE_SIZE runs under DIR into "
+                         "profiles/traffic.json")
     args = ap.parse_args()
+    if args.record_traffic:
+        print(json.dumps(record_traffic(Path(args.record_traffic)), indent=1))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this attention library runs on one GPU; --gpus must be 1"}))
