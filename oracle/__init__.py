@@ -112,6 +112,28 @@ class Oracle:
         self.threads_used = ret
         return out
 
+    def prefill_varlen(self, q, k, v, cu_seqlens, *, scale: float, causal: bool = False, window: int = 0,
+                       nthreads: int | None = None) -> np.ndarray:
+        """Unpadded batch (ripvec-core `Driver`, `prepare_batch_unpadded`): tokens of all
+        items concatenated, token-major q [T,Hq,D], k/v [T,Hkv,D]; item b is tokens
+        [cu_seqlens[b], cu_seqlens[b+1]) and attends over its own tokens only, query i at
+        position i.  Returns [T,Hq,D] float64; rows of no item stay 0."""
+        q, k, v = (np.ascontiguousarray(x) for x in (q, k, v))
+        T, Hq, D = q.shape
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        out = np.zeros((T, Hq, D), np.float64)
+        for b in range(len(cu) - 1):
+            t0, t1 = int(cu[b]), int(cu[b + 1])
+            if t1 <= t0:
+                continue
+            # this item alone in the head-major layout [1, heads, len, D]
+            qi = np.ascontiguousarray(q[t0:t1].transpose(1, 0, 2))[None]
+            ki = np.ascontiguousarray(k[t0:t1].transpose(1, 0, 2))[None]
+            vi = np.ascontiguousarray(v[t0:t1].transpose(1, 0, 2))[None]
+            oi = self.prefill(qi, ki, vi, scale=scale, causal=causal, window=window, nthreads=nthreads)
+            out[t0:t1] = oi[0].transpose(1, 0, 2)
+        return out
+
     # ---- decode ----------------------------------------------------------------
     def decode(self, q, k_cache, v_cache, *, kv_len: int, scale: float, pos_offset: int = 0,
                kv_lens=None, window: int = 0, rows=None, nthreads: int | None = None) -> np.ndarray:

@@ -510,4 +510,63 @@ def pin_decode_per_cache_equals_single_calls(oracle):
             _close(out[b], np.array(ref[0]), 1e-12, f"per-cache brute item {b} W={W}")
 
 
+# ---------------------------------------------------------------------------
+# unpadded (varlen) batches (ripvec-core `Driver`, `prepare_batch_unpadded`)
+
+def pin_varlen_brute_force(oracle):
+    """Token-major unpadded batch == brute force on each item's own tokens, with the
+    item's rows gathered by explicit per-token loops (not by a reshape)."""
+    for n, (lens, Hq, Hkv, D, causal, W) in enumerate([
+            ([3, 0, 5, 1], 2, 1, 4, True, 0),
+            ([6, 2], 4, 2, 8, False, 0),
+            ([5, 4, 7], 2, 2, 4, False, 3),
+            ([7, 1, 4], 2, 1, 8, True, 3)]):
+        rng = _rng(540 + n)
+        T = sum(lens)
+        q = draw(rng, (T, Hq, D), 1.0, "f32")
+        k = draw(rng, (T, Hkv, D), 1.0, "f32")
+        v = draw(rng, (T, Hkv, D), 1.0, "f32")
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        got = oracle.prefill_varlen(q, k, v, cu, scale=0.55, causal=causal, window=W)
+        for b, L in enumerate(lens):
+            if L == 0:
+                continue
+            t0 = int(cu[b])
+            qi = np.zeros((1, Hq, L, D), np.float32)
+            ki = np.zeros((1, Hkv, L, D), np.float32)
+            vi = np.zeros((1, Hkv, L, D), np.float32)
+            for t in range(L):
+                for h in range(Hq):
+                    qi[0, h, t] = q[t0 + t, h]
+                for h in range(Hkv):
+                    ki[0, h, t] = k[t0 + t, h]
+                    vi[0, h, t] = v[t0 + t, h]
+            ref = np.array(brute.attention(qi, ki, vi, scale=0.55, causal=causal, window=W))
+            for t in range(L):
+                for h in range(Hq):
+                    _close(got[t0 + t, h], ref[0, h, t], 1e-12, f"varlen case {n} item {b} token {t} head {h}")
+
+
+def pin_varlen_item_order(oracle):
+    """Reordering the items (moving each item's token block with it) reorders the output
+    blocks the same way; a single-token item outputs its own V row."""
+    rng = _rng(550)
+    lens = [4, 1, 6]
+    Hq, Hkv, D = 4, 2, 8
+    T = sum(lens)
+    q = draw(rng, (T, Hq, D), 1.0, "bf16")
+    k = draw(rng, (T, Hkv, D), 1.0, "bf16")
+    v = draw(rng, (T, Hkv, D), 1.0, "bf16")
+    cu = np.array([0, 4, 5, 11], np.int32)
+    a = oracle.prefill_varlen(q, k, v, cu, scale=0.4, causal=True)
+    order = [2, 0, 1]
+    blocks = [np.arange(cu[b], cu[b + 1]) for b in order]
+    idx = np.concatenate(blocks)
+    cu2 = np.concatenate([[0], np.cumsum([lens[b] for b in order])]).astype(np.int32)
+    b2 = oracle.prefill_varlen(q[idx], k[idx], v[idx], cu2, scale=0.4, causal=True)
+    _close(b2, a[idx], 0.0, "item reorder")
+    for h in range(Hq):
+        _close(a[4, h], _f64(v[4, h // 2]), 0.0, "single-token item")
+
+
 PINS = {name[4:]: fn for name, fn in sorted(globals().items()) if name.startswith("pin_") and callable(fn)}

@@ -106,8 +106,34 @@ class _PerCacheItemsRotated(oracle.Oracle):
         return oracle.Oracle.decode_per_cache(self, q, k, v, kv_lens, scale=scale, window=window)
 
 
+class _VarlenItemOneLonger(oracle.Oracle):
+    def prefill_varlen(self, q, k, v, cu_seqlens, *, scale, causal=False, window=0, nthreads=None):
+        cu = np.array(cu_seqlens, np.int64)
+        cu[1:-1] += 1
+        return oracle.Oracle.prefill_varlen(self, q, k, v, cu, scale=scale, causal=causal, window=window)
+
+
+class _VarlenHeadsAsTokens(oracle.Oracle):
+    def prefill_varlen(self, q, k, v, cu_seqlens, *, scale, causal=False, window=0, nthreads=None):
+        T, Hq, D = q.shape
+        out = np.zeros((T, Hq, D))
+        cu = np.asarray(cu_seqlens, np.int64)
+        for b in range(len(cu) - 1):
+            t0, t1 = int(cu[b]), int(cu[b + 1])
+            if t1 <= t0:
+                continue
+            L = t1 - t0
+            qi = np.ascontiguousarray(q[t0:t1]).reshape(1, Hq, L, D)     # reshape, no transpose
+            ki = np.ascontiguousarray(k[t0:t1]).reshape(1, k.shape[1], L, D)
+            vi = np.ascontiguousarray(v[t0:t1]).reshape(1, v.shape[1], L, D)
+            oi = self.prefill(qi, ki, vi, scale=scale, causal=causal, window=window)
+            out[t0:t1] = oi[0].reshape(L, Hq, D)
+        return out
+
+
 PY_MUTANTS = {c.__name__[1:]: c for c in (_AppendOneLate, _AppendKVSwapped, _AppendModifiesInput,
-                                          _NewKeyNotAttended, _NoRoomAttendsAll, _PerCacheItemsRotated)}
+                                          _NewKeyNotAttended, _NoRoomAttendsAll, _PerCacheItemsRotated,
+                                          _VarlenItemOneLonger, _VarlenHeadsAsTokens)}
 
 
 @pytest.mark.parametrize("name", sorted(PY_MUTANTS))
