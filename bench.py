@@ -74,6 +74,8 @@ def prefill_flops(w: W.Workload, seq_lens) -> float:
 def prefill_bytes(w: W.Workload, seq_lens) -> float:
     """Q + valid K/V rows + O, each once."""
     esz = 2 if w.dtype == "bf16" else 4
+    if w.kind == "prefill_varlen":   # every token row is an item's
+        return 2.0 * (w.q_heads + w.kv_heads) * w.head_dim * esz * float(np.sum(seq_lens))
     valid = np.full(w.batch, w.kv_len) if seq_lens is None else np.clip(seq_lens, 0, w.kv_len)
     kv = 2.0 * w.kv_heads * w.head_dim * esz * float(valid.sum())
     qo = 2.0 * w.batch * w.q_heads * w.q_len * w.head_dim * esz
@@ -113,6 +115,9 @@ class Runner:
         self.q, self.k, self.v = to_gpu(x["q"]), to_gpu(x["k"]), to_gpu(x["v"])
         self.out = torch.empty_like(self.q)
         lens = x.get("seq_lens") if w.kind == "prefill" else x.get("kv_lens")
+        if w.kind == "prefill_varlen":
+            self.cu = to_gpu(x["cu_seqlens"])
+            self.max_seqlen = int(np.max(x["seq_lens"]))
         self.lens = None if lens is None else to_gpu(lens)
         self.ws = None
         if w.kind in ("decode", "decode_append"):
@@ -128,6 +133,9 @@ class Runner:
         if w.kind == "prefill":
             self.mi.attn_prefill(self.q, self.k, self.v, self.out, pos_offset=w.pos_offset, seq_lens=self.lens,
                                  window=w.window, causal=w.causal, scale=w.attn_scale)
+        elif w.kind == "prefill_varlen":
+            self.mi.attn_prefill_varlen(self.q, self.k, self.v, self.cu, self.max_seqlen, self.out, window=w.window,
+                                        causal=w.causal, scale=w.attn_scale)
         elif w.kind == "decode_append":
             # the same slot is rewritten every step (the lengths are not advanced), so
             # every step does the same work
@@ -161,8 +169,34 @@ def traffic_from_profiles(key: str, digest: str):
 # CPU baseline: the oracle, timed on the host cores on a bounded sample
 
 
+def cpu_baseline_varlen(w: W.Workload, x: dict, budget_s: float) -> dict:
+    """The oracle on the first n items of the unpadded batch (whole items: the oracle
+    has no per-row entry for this layout)."""
+    import oracle
+    ref = oracle.default()
+    nt = len(os.sched_getaffinity(0))
+    lens, cu = np.asarray(x["seq_lens"], np.int64), np.asarray(x["cu_seqlens"], np.int64)
+    n = 1
+    while True:
+        T = int(cu[n])
+        t0 = time.perf_counter()
+        ref.prefill_varlen(x["q"][:T], x["k"][:T], x["v"][:T], cu[:n + 1].astype(np.int32), scale=w.attn_scale,
+                           causal=w.causal, window=w.window, nthreads=nt)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 4 or n == w.batch:
+            break
+        n = min(w.batch, max(n * 2, int(n * budget_s / max(dt, 1e-3))))
+    sub = W.Workload(w.name, "prefill", n, w.q_heads, w.kv_heads, w.q_len, w.kv_len, w.head_dim, w.dtype, w.sigma,
+                     w.causal, window=w.window)
+    flops = prefill_flops(sub, lens[:n])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": ref.threads_used, "kind": "oracle",
+            "sample": f"the first {n} of {w.batch} items of {w.name} ({T} tokens), fp64, {dt:.1f} s"}
+
+
 def cpu_baseline_prefill(w: W.Workload, x: dict, budget_s: float) -> dict:
     import oracle
+    if w.kind == "prefill_varlen":
+        return cpu_baseline_varlen(w, x, budget_s)
     ref = oracle.default()
     nt = len(os.sched_getaffinity(0))
     rng = np.random.default_rng(123)
@@ -378,7 +412,7 @@ def main() -> int:
     rooflines = {}
     for w, x, ms in zip(ws, inputs, kernel_ms):
         sec = ms / 1e3
-        if w.kind == "prefill":
+        if w.kind in ("prefill", "prefill_varlen"):
             fl = prefill_flops(w, x["seq_lens"])
             peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
             if w.dtype != "bf16":
@@ -422,7 +456,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (cpu_baseline)")
         for w, x in zip(ws, inputs):
-            if w.kind == "prefill":
+            if w.kind in ("prefill", "prefill_varlen"):
                 result.setdefault("cpu_baseline", cpu_baseline_prefill(w, x, args.cpu_budget))
             else:
                 key = "cpu_baseline" if "cpu_baseline" not in result else "cpu_baseline_decode"

@@ -8,6 +8,8 @@ missing library or GPU raises.
 
     attn_prefill(q, k, v, out=None, *, pos_offset=0, seq_lens=None, window=0,
                  causal=False, scale=None)
+    attn_prefill_varlen(q, k, v, cu_seqlens, max_seqlen=None, out=None, *, window=0,
+                        causal=False, scale=None)
     attn_decode(q, k_cache, v_cache, out=None, *, kv_len=None, pos_offset=None,
                 kv_lens=None, window=0, scale=None, workspace=None)
     attn_decode_per_cache(q, k_caches, v_caches, kv_lens, out=None, *, window=0,
@@ -17,7 +19,8 @@ missing library or GPU raises.
     attn_decode_workspace_bytes(batch, q_heads, kv_heads, kv_len, head_dim)
     attn_last_error(), attn_version()
 
-Layouts: q [batch, q_heads, q_len, head_dim]; k, v [batch, kv_heads, kv_len, head_dim];
+Layouts: q [batch, q_heads, q_len, head_dim]; k, v [batch, kv_heads, kv_len, head_dim]
+(unpadded: q, out [tokens, q_heads, head_dim], k, v [tokens, kv_heads, head_dim]);
 decode caches [batch, kv_heads, capacity, head_dim] (head-major); the per-cache calls
 take one [kv_heads, capacity, head_dim] cache per item.  scale defaults to
 1/sqrt(head_dim).
@@ -33,7 +36,7 @@ LIBRARY = Path(__file__).resolve().parent / "libmi_attn.so"
 MI_ATTN_F32, MI_ATTN_BF16 = 0, 1
 MI_ATTN_OK, MI_ATTN_ERR_INVALID, MI_ATTN_ERR_UNSUPPORTED, MI_ATTN_ERR_HIP = 0, 1, 2, 3
 
-EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_per_cache", "attn_decode_append",
+EXPORTS = ("attn_prefill", "attn_prefill_varlen", "attn_decode", "attn_decode_per_cache", "attn_decode_append",
            "attn_decode_workspace_bytes", "attn_last_error", "attn_version")
 
 
@@ -56,6 +59,8 @@ def library() -> ctypes.CDLL:
         vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         lib.attn_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, i, i, f, i, vp]
         lib.attn_prefill.restype = i
+        lib.attn_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+        lib.attn_prefill_varlen.restype = i
         lib.attn_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, i, f, i, vp, sz, vp]
         lib.attn_decode.restype = i
         lib.attn_decode_per_cache.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, i, f, i, vp, sz, vp]
@@ -147,6 +152,39 @@ def attn_prefill(q, k, v, out=None, *, pos_offset: int = 0, seq_lens=None, windo
     st = library().attn_prefill(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), B, Hq, Hkv, Lq, Lk,
                                 D, pos_offset, _dev(seq_lens, "seq_lens"), window, int(bool(causal)),
                                 float(scale), dt, _stream(stream))
+    _check(st)
+    return out
+
+
+def attn_prefill_varlen(q, k, v, cu_seqlens, max_seqlen: int | None = None, out=None, *, window: int = 0,
+                        causal: bool = False, scale: float | None = None, stream=None):
+    """Prefill on an unpadded, token-major batch; returns `out` [tokens, q_heads, head_dim].
+    Without `max_seqlen` it is read from cu_seqlens on the host (one device sync)."""
+    torch = _torch()
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("q must be [tokens,Hq,D] and k, v [tokens,Hkv,D]")
+    T, Hq, D = q.shape
+    Tk, Hkv, Dk = k.shape
+    if Tk != T or Dk != D:
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree on tokens or head_dim")
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor of batch + 1 offsets")
+    B = cu_seqlens.numel() - 1
+    if max_seqlen is None:
+        c = cu_seqlens.cpu()
+        max_seqlen = int((c[1:] - c[:-1]).max()) if B > 0 else 0
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = library().attn_prefill_varlen(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                                       _dev(cu_seqlens, "cu_seqlens"), B, int(max_seqlen), Hq, Hkv, D, window,
+                                       int(bool(causal)), float(scale), dt, _stream(stream))
     _check(st)
     return out
 

@@ -88,6 +88,55 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int bat
     return MI_ATTN_OK;
 }
 
+int attn_prefill_varlen(const void* q, const void* k, const void* v, void* out, const int32_t* cu_seqlens,
+                        int batch, int max_seqlen, int q_heads, int kv_heads, int head_dim, int window, int causal,
+                        float scale, int dtype, void* stream) {
+    g_error[0] = '\0';
+    const char* fn = "attn_prefill_varlen";
+    if (dtype != MI_ATTN_BF16 && dtype != MI_ATTN_F32)
+        return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+    if (batch < 0 || max_seqlen < 0)
+        return fail(MI_ATTN_ERR_INVALID, "%s: negative size (batch %d, max_seqlen %d)", fn, batch, max_seqlen);
+    if (q_heads < 1 || kv_heads < 1)
+        return fail(MI_ATTN_ERR_INVALID, "%s: q_heads (%d) and kv_heads (%d) must be >= 1", fn, q_heads,
+                    kv_heads);
+    if (q_heads % kv_heads != 0)
+        return fail(MI_ATTN_ERR_INVALID, "%s: q_heads (%d) is not a multiple of kv_heads (%d)", fn, q_heads,
+                    kv_heads);
+    if (window < 0) return fail(MI_ATTN_ERR_INVALID, "%s: window (%d) is negative", fn, window);
+    if (!std::isfinite(scale)) return fail(MI_ATTN_ERR_INVALID, "%s: scale is not finite", fn);
+    if (!supported_head_dim(head_dim))
+        return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: head_dim %d is not one of 32, 64, 128", fn, head_dim);
+    if (batch == 0 || max_seqlen == 0) return MI_ATTN_OK;
+    if (!q || !k || !v || !out || !cu_seqlens) return fail(MI_ATTN_ERR_INVALID, "%s: null pointer argument", fn);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(MI_ATTN_ERR_INVALID, "%s: tensors must be 16-byte aligned", fn);
+    if ((uintptr_t)cu_seqlens & 3u) return fail(MI_ATTN_ERR_INVALID, "%s: cu_seqlens must be 4-byte aligned", fn);
+    if ((long)q_heads > 65535 || (long)batch > 65535)
+        return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: q_heads and batch must be <= 65535", fn);
+
+    mi_attn::PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.cu_seqlens = cu_seqlens;
+    a.batch = batch;
+    a.q_heads = q_heads;
+    a.kv_heads = kv_heads;
+    a.q_len = max_seqlen;
+    a.kv_len = max_seqlen;
+    a.pos_offset = 0;
+    a.window = window;
+    a.causal = causal ? 1 : 0;
+    a.scale = scale;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = dtype == MI_ATTN_BF16 ? mi_attn::launch_prefill_bf16(a, head_dim, s)
+                                         : mi_attn::launch_prefill_f32(a, head_dim, s);
+    if (e != hipSuccess) return fail(MI_ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return MI_ATTN_OK;
+}
+
 size_t attn_decode_workspace_bytes(int batch, int q_heads, int kv_heads, int kv_len, int head_dim) {
     if (batch <= 0 || q_heads < 1 || kv_heads < 1 || q_heads % kv_heads || kv_len < 1 ||
         !supported_head_dim(head_dim))

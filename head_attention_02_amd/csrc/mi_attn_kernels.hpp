@@ -7,18 +7,55 @@
 
 namespace mi_attn {
 
-// One prefill problem, as validated by attn_prefill.
+// One prefill problem, as validated by attn_prefill or attn_prefill_varlen.
 struct PrefillArgs {
     const void* q;
     const void* k;
     const void* v;
     void* out;
     const int32_t* seq_lens;  // device [batch] or nullptr
+    // Unpadded (varlen) layout: device [batch + 1] token offsets; q and out are then
+    // [tokens, q_heads, D] and k, v [tokens, kv_heads, D] (token-major), item b holds
+    // tokens [cu_seqlens[b], cu_seqlens[b+1]) and q_len is the longest item.  nullptr:
+    // the padded head-major layout [batch, heads, len, D].
+    const int32_t* cu_seqlens;
     int batch, q_heads, kv_heads, q_len, kv_len;
     int pos_offset, window, causal;
     float scale;
     int n_qtiles;             // grid.x
 };
+
+// Where one (item, query head)'s rows live and how many there are (element offsets and
+// strides; the same code serves both layouts).
+struct ItemRows {
+    size_t q_base;    // row 0 of (item, query head) in q and out
+    size_t kv_base;   // row 0 of (item, kv head) in k and v
+    int q_rs, kv_rs;  // elements from one row to the next
+    int q_len;        // query rows of the item
+    int kv_valid;     // keys of the item (seq_lens applied)
+};
+
+__device__ __forceinline__ ItemRows item_rows(const PrefillArgs& a, int b, int h, int kvh, int D) {
+    ItemRows r;
+    if (a.cu_seqlens) {
+        const int t0 = a.cu_seqlens[b];
+        const int n = min(max(a.cu_seqlens[b + 1] - t0, 0), a.q_len);
+        r.q_rs = a.q_heads * D;
+        r.kv_rs = a.kv_heads * D;
+        r.q_base = (size_t)t0 * r.q_rs + (size_t)h * D;
+        r.kv_base = (size_t)t0 * r.kv_rs + (size_t)kvh * D;
+        r.q_len = n;
+        r.kv_valid = n;
+    } else {
+        r.q_rs = D;
+        r.kv_rs = D;
+        r.q_base = ((size_t)b * a.q_heads + h) * (size_t)a.q_len * D;
+        r.kv_base = ((size_t)b * a.kv_heads + kvh) * (size_t)a.kv_len * D;
+        r.q_len = a.q_len;
+        r.kv_valid = a.seq_lens ? min(max(a.seq_lens[b], 0), a.kv_len) : a.kv_len;
+    }
+    return r;
+}
 
 // One decode problem, as validated and planned by attn_decode.
 struct DecodeArgs {

@@ -120,6 +120,7 @@ struct Prefill {
     int lane, wave, g;
     int cw;                     // index among the copying waves (group 1)
     int kvalid;                 // valid key rows of this item
+    int kv_rs;                  // elements from one K/V row to the next
     const char* kg;             // K rows of this (item, kv head)
     const char* vg;
     uint32_t k_lds0, v_lds0;    // LDS byte addresses of buffer 0
@@ -144,14 +145,14 @@ struct Prefill {
     // f fills block f: lane p reads key 32kb2 + p%32 at chunk 2kc + p/32, i.e. a per-lane
     // offset ((p%32)*D + 8*(p/32))*2 plus a per-copy base (32*kb2*D + 16*kc)*2.
     __device__ __forceinline__ void copy_k(int kt, int par) const {
-        const char* base = kg + (size_t)kt * kBN * D * 2;
+        const char* base = kg + (size_t)kt * kBN * kv_rs * 2;
         const bool tail = kt * kBN + kBN > kvalid;
 #pragma unroll
         for (int ii = 0; ii < G::NKW; ++ii) {
             const int f = cw + kCopyWaves * ii;
             if (f < G::NK) {
                 const int kb2 = f / G::KC, kc = f % G::KC;
-                const char* b = base + (32 * kb2 * D + 16 * kc) * 2;
+                const char* b = base + ((size_t)32 * kb2 * kv_rs + 16 * kc) * 2;
                 uint32_t off = k_off;
                 if (tail) {
                     // keys past the valid length repeat the last valid key; the clamped key
@@ -159,7 +160,7 @@ struct Prefill {
                     // tile count guarantees kvalid - 1 - kt*64 >= 0)
                     const int row = min(32 * kb2 + (lane & 31), kvalid - 1 - kt * kBN);
                     b = base;
-                    off = (uint32_t)((row * D + 16 * kc + 8 * (lane >> 5)) * 2);
+                    off = (uint32_t)((row * kv_rs + 16 * kc + 8 * (lane >> 5)) * 2);
                 }
                 lds_dma16(b, off, k_lds0 + par * G::K_BYTES + f * 1024);
             }
@@ -174,21 +175,21 @@ struct Prefill {
     // 16c4 + 8hi + 4(q/16) + (q%8)/2 at dims 32db + 16((q/8)%2) + 8(q%2) -- a per-lane
     // offset plus a per-copy base (16c4*D + 32db)*2.
     __device__ __forceinline__ void copy_v(int kt, int par) const {
-        const char* base = vg + (size_t)kt * kBN * D * 2;
+        const char* base = vg + (size_t)kt * kBN * kv_rs * 2;
         const bool tail = kt * kBN + kBN > kvalid;
 #pragma unroll
         for (int ii = 0; ii < G::NVW; ++ii) {
             const int j = cw + kCopyWaves * ii;
             if (j < G::NV) {
                 const int c4 = j / G::DB, db = j % G::DB;
-                const char* b = base + (16 * c4 * D + 32 * db) * 2;
+                const char* b = base + ((size_t)16 * c4 * kv_rs + 32 * db) * 2;
                 uint32_t off = v_off;
                 if (tail) {   // as for K: clamp, and address from the tile base
                     const int q = lane & 31;
                     const int r = 8 * (lane >> 5) + 4 * (q >> 4) + ((q & 7) >> 1);
                     const int row = min(16 * c4 + r, kvalid - 1 - kt * kBN);
                     b = base;
-                    off = (uint32_t)((row * D + 32 * db + 16 * ((q >> 3) & 1) + 8 * (q & 1)) * 2);
+                    off = (uint32_t)((row * kv_rs + 32 * db + 16 * ((q >> 3) & 1) + 8 * (q & 1)) * 2);
                 }
                 lds_dma16(b, off, v_lds0 + par * G::V_BYTES + j * 1024);
             }
@@ -376,12 +377,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     const int qt = a.causal ? (a.n_qtiles - 1 - qt_rank) : qt_rank;
     const int kvh = h / qgrp;
 
-    int valid = a.kv_len;
-    if (a.seq_lens) valid = min(max(a.seq_lens[b], 0), a.kv_len);
+    const ItemRows ir = item_rows(a, b, h, kvh, D);
+    const int valid = ir.kv_valid;
+    const int q_len = ir.q_len;
     st.kvalid = valid;
+    st.kv_rs = ir.kv_rs;
 
     const int q0 = qt * kBM;
-    const int last_row = min(q0 + kBM, a.q_len) - 1;
+    if (q0 >= q_len) return;   // no query row of this item in the tile (unpadded layout)
+    const int last_row = min(q0 + kBM, q_len) - 1;
     const int half_w = a.window / 2;
 
     // ---- key range of the whole workgroup -------------------------------------------
@@ -417,11 +421,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
                 hi_r = min(hi_r, my_pos + half_w);
             }
         }
-        if (my_pos >= valid || my_row >= a.q_len) hi_r = -1;
+        if (my_pos >= valid || my_row >= q_len) hi_r = -1;
         st.lo_r = lo_r;
         st.hi_r = hi_r;
 
-        const int r1 = min(r0 + 31, a.q_len - 1);
+        const int r1 = min(r0 + 31, q_len - 1);
         const int bp_lo = a.pos_offset + r0, bp_hi = a.pos_offset + r1;
         int inter_lo = 0, inter_hi = valid - 1;
         if (a.causal) inter_hi = min(inter_hi, bp_lo);
@@ -445,17 +449,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
                 union_hi = min(union_hi, bp_hi + half_w);
             }
         }
-        if (r0 >= a.q_len || bp_lo >= valid) union_hi = -1;   // no row of the wave is a query
+        if (r0 >= q_len || bp_lo >= valid) union_hi = -1;   // no row of the wave is a query
         st.union_lo = union_lo;
         st.union_hi = union_hi;
-        st.all_rows_valid = r0 < a.q_len && bp_hi < valid;
+        st.all_rows_valid = r0 < q_len && bp_hi < valid;
     }
 
     // ---- Q^T operand: lane l holds row l%32, dims 16*kc + 8*g + [0, 8) ---------------
-    const size_t q_head = ((size_t)b * a.q_heads + h) * (size_t)a.q_len;
     {
-        const uint16_t* qrow = (const uint16_t*)a.q + (q_head + (size_t)min(my_row, a.q_len - 1)) * D;
-        const bool in = my_row < a.q_len;
+        const uint16_t* qrow = (const uint16_t*)a.q + ir.q_base + (size_t)min(my_row, q_len - 1) * ir.q_rs;
+        const bool in = my_row < q_len;
 #pragma unroll
         for (int kc = 0; kc < G::KC; ++kc) {
             u32x4 w = in ? *(const u32x4*)(qrow + 16 * kc + 8 * g) : u32x4{0, 0, 0, 0};
@@ -467,16 +470,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     // placing its own wait for Q inside the loop, where it would also wait for the tile
     // copies in flight.
 
-    const size_t kv_head = ((size_t)b * a.kv_heads + kvh) * (size_t)a.kv_len;
-    st.kg = (const char*)((const uint16_t*)a.k + kv_head * D);
-    st.vg = (const char*)((const uint16_t*)a.v + kv_head * D);
+    st.kg = (const char*)((const uint16_t*)a.k + ir.kv_base);
+    st.vg = (const char*)((const uint16_t*)a.v + ir.kv_base);
     st.k_lds0 = lds_addr(k_lds[0]);
     st.v_lds0 = lds_addr(v_lds[0]);
-    st.k_off = (uint32_t)(((lane & 31) * D + 8 * (lane >> 5)) * 2);
+    st.k_off = (uint32_t)(((lane & 31) * ir.kv_rs + 8 * (lane >> 5)) * 2);
     {
         const int q = lane & 31;
         const int r = 8 * (lane >> 5) + 4 * (q >> 4) + ((q & 7) >> 1);
-        st.v_off = (uint32_t)((r * D + 16 * ((q >> 3) & 1) + 8 * (q & 1)) * 2);
+        st.v_off = (uint32_t)((r * ir.kv_rs + 16 * ((q >> 3) & 1) + 8 * (q & 1)) * 2);
     }
     st.c2 = a.scale * kLog2e;
 #pragma unroll
@@ -551,9 +553,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
 
     // ---- epilogue: normalise, zero padded / empty rows, store bf16 --------------------
     const float l_tot = halves_sum(st.l_run);
-    if (my_row >= a.q_len) return;
+    if (my_row >= q_len) return;
     const float inv = (st.hi_r >= 0 && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
-    uint16_t* orow = (uint16_t*)a.out + (q_head + (size_t)my_row) * D;
+    uint16_t* orow = (uint16_t*)a.out + ir.q_base + (size_t)my_row * ir.q_rs;
 #pragma unroll
     for (int db = 0; db < G::DB; ++db) {
 #pragma unroll

@@ -113,6 +113,7 @@ struct Prefill {
     // ---- per-lane constants ---------------------------------------------------------
     int lane, wave, g;
     int kvalid;                 // valid key rows of this item
+    int kv_rs;                  // elements from one K/V row to the next
     const char* kg;             // K rows of this (item, kv head)
     const char* vg;
     uint32_t k_lds0, v_lds0;    // LDS byte addresses of buffer 0
@@ -131,7 +132,7 @@ struct Prefill {
     float m_run[RB], l_run[RB];
 
     __device__ __forceinline__ void copy_k(int kt, int par) {
-        const char* base = kg + (size_t)kt * kBN * D * 2;
+        const char* base = kg + (size_t)kt * kBN * kv_rs * 2;
         const bool tail = kt * kBN + kBN > kvalid;
 #pragma unroll
         for (int ii = 0; ii < G::NKW; ++ii) {
@@ -143,7 +144,7 @@ struct Prefill {
                     int row = p / G::KS, c = p - (p / G::KS) * G::KS;
                     c = c < G::CPR ? c : 0;
                     row = min(row, kvalid - 1 - kt * kBN);
-                    off = (uint32_t)((row * D + c * 8) * 2);
+                    off = (uint32_t)((row * kv_rs + c * 8) * 2);
                 }
                 lds_dma16(base, off, k_lds0 + par * G::K_BYTES + i * 1024);
             }
@@ -151,19 +152,21 @@ struct Prefill {
     }
 
     __device__ __forceinline__ void copy_v(int kt, int par) {
-        const char* base = vg + (size_t)kt * kBN * D * 2;
+        const char* base = vg + (size_t)kt * kBN * kv_rs * 2;
         const bool tail = kt * kBN + kBN > kvalid;
 #pragma unroll
         for (int ii = 0; ii < G::NVW; ++ii) {
             const int i = wave + W * ii;
             uint32_t off = voff;
-            const char* b = base + ii * (W * 1024);
+            // copy ii covers the rows W*64/CPR further down than copy ii-1 (same lane
+            // offsets: the swizzle repeats with that period)
+            const char* b = base + (size_t)ii * (W * 64 / G::CPR) * kv_rs * 2;
             if (tail) {
                 const int p = i * 64 + lane;
                 int row = p / G::CPR;
                 const int c = (p % G::CPR) ^ vswz<D>(row);
                 row = min(row, kvalid - 1 - kt * kBN);
-                off = (uint32_t)((row * D + c * 8) * 2);
+                off = (uint32_t)((row * kv_rs + c * 8) * 2);
                 b = base;
             }
             lds_dma16(b, off, v_lds0 + par * G::V_BYTES + i * 1024);
@@ -418,12 +421,15 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
     const int qt = a.causal ? (a.n_qtiles - 1 - qt_rank) : qt_rank;
     const int kvh = h / grp;
 
-    int valid = a.kv_len;
-    if (a.seq_lens) valid = min(max(a.seq_lens[b], 0), a.kv_len);
+    const ItemRows ir = item_rows(a, b, h, kvh, D);
+    const int valid = ir.kv_valid;
+    const int q_len = ir.q_len;
     st.kvalid = valid;
+    st.kv_rs = ir.kv_rs;
 
     const int q0 = qt * BM;
-    const int last_row = min(q0 + BM, a.q_len) - 1;
+    if (q0 >= q_len) return;   // no query row of this item in the tile (unpadded layout)
+    const int last_row = min(q0 + BM, q_len) - 1;
     const int half_w = a.window / 2;
 
     // ---- key range of the whole workgroup -------------------------------------------
@@ -461,11 +467,11 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
                 hi_r = min(hi_r, my_pos + half_w);
             }
         }
-        if (my_pos >= valid || my_row[rb] >= a.q_len) hi_r = -1;
+        if (my_pos >= valid || my_row[rb] >= q_len) hi_r = -1;
         st.lo_r[rb] = lo_r;
         st.hi_r[rb] = hi_r;
 
-        const int r1 = min(r0 + 31, a.q_len - 1);
+        const int r1 = min(r0 + 31, q_len - 1);
         const int bp_lo = a.pos_offset + r0, bp_hi = a.pos_offset + r1;
         int inter_lo = 0, inter_hi = valid - 1;
         if (a.causal) inter_hi = min(inter_hi, bp_lo);
@@ -479,15 +485,14 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
         }
         st.b_inter_lo[rb] = inter_lo;
         st.b_inter_hi[rb] = inter_hi;
-        st.blk_all_rows_valid[rb] = r0 < a.q_len && bp_hi < valid;
+        st.blk_all_rows_valid[rb] = r0 < q_len && bp_hi < valid;
     }
 
     // ---- Q^T operands: lane l holds row l%32 of each block, dims 16*kc + 8*g + [0, 8)
-    const size_t q_head = ((size_t)b * a.q_heads + h) * (size_t)a.q_len;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        const uint16_t* qrow = (const uint16_t*)a.q + (q_head + (size_t)min(my_row[rb], a.q_len - 1)) * D;
-        const bool in = my_row[rb] < a.q_len;
+        const uint16_t* qrow = (const uint16_t*)a.q + ir.q_base + (size_t)min(my_row[rb], q_len - 1) * ir.q_rs;
+        const bool in = my_row[rb] < q_len;
 #pragma unroll
         for (int kc = 0; kc < G::KC; ++kc) {
             u32x4 w = in ? *(const u32x4*)(qrow + 16 * kc + 8 * g) : u32x4{0, 0, 0, 0};
@@ -499,9 +504,8 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
     // placing its own wait for Q inside the loop, where it would also wait for the next
     // tile's copy.
 
-    const size_t kv_head = ((size_t)b * a.kv_heads + kvh) * (size_t)a.kv_len;
-    st.kg = (const char*)((const uint16_t*)a.k + kv_head * D);
-    st.vg = (const char*)((const uint16_t*)a.v + kv_head * D);
+    st.kg = (const char*)((const uint16_t*)a.k + ir.kv_base);
+    st.vg = (const char*)((const uint16_t*)a.v + ir.kv_base);
     st.k_lds0 = lds_addr(k_lds[0]);
     st.v_lds0 = lds_addr(v_lds[0]);
 #pragma unroll
@@ -510,13 +514,13 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
         const int row = p / G::KS;
         int c = p - row * G::KS;
         c = c < G::CPR ? c : 0;
-        st.koff[ii] = (uint32_t)((row * D + c * 8) * 2);
+        st.koff[ii] = (uint32_t)((row * ir.kv_rs + c * 8) * 2);
     }
     {
         const int p = wave * 64 + lane;
         const int row = p / G::CPR;
         const int c = (p % G::CPR) ^ vswz<D>(row);
-        st.voff = (uint32_t)((row * D + c * 8) * 2);
+        st.voff = (uint32_t)((row * ir.kv_rs + c * 8) * 2);
     }
     st.k_read = ((lane & 31) * G::KS + g) * 16;
     {
@@ -587,9 +591,9 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const float l_tot = halves_sum(st.l_run[rb]);
-        if (my_row[rb] < a.q_len) {
+        if (my_row[rb] < q_len) {
             const float inv = (st.hi_r[rb] >= 0 && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
-            uint16_t* orow = (uint16_t*)a.out + (q_head + (size_t)my_row[rb]) * D;
+            uint16_t* orow = (uint16_t*)a.out + ir.q_base + (size_t)my_row[rb] * ir.q_rs;
 #pragma unroll
             for (int db = 0; db < G::DB; ++db) {
 #pragma unroll

@@ -24,11 +24,13 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
     const int qt = a.causal ? (a.n_qtiles - 1 - (int)blockIdx.x) : (int)blockIdx.x;
     const int kvh = h / (a.q_heads / a.kv_heads);
 
-    int valid = a.kv_len;
-    if (a.seq_lens) valid = min(max(a.seq_lens[b], 0), a.kv_len);
+    const ItemRows ir = item_rows(a, b, h, kvh, D);
+    const int valid = ir.kv_valid;
+    const int q_len = ir.q_len;
 
     const int q0 = qt * kRows;
-    const int last_row = min(q0 + kRows, a.q_len) - 1;
+    if (q0 >= q_len) return;   // no query row of this item in the tile (unpadded layout)
+    const int last_row = min(q0 + kRows, q_len) - 1;
     const int half_w = a.window / 2;
     const int p_lo = a.pos_offset + q0, p_hi = a.pos_offset + last_row;
     int k_begin = 0, k_end = valid;
@@ -55,19 +57,17 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
             hi_r = min(hi_r, pos + half_w);
         }
     }
-    if (pos >= valid || row >= a.q_len) hi_r = -1;
+    if (pos >= valid || row >= q_len) hi_r = -1;
 
-    const size_t q_head = ((size_t)b * a.q_heads + h) * (size_t)a.q_len;
-    const float* qrow = (const float*)a.q + (q_head + (size_t)min(row, a.q_len - 1)) * D;
+    const float* qrow = (const float*)a.q + ir.q_base + (size_t)min(row, q_len - 1) * ir.q_rs;
     float q[D], o[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-        q[d] = row < a.q_len ? qrow[d] : 0.0f;
+        q[d] = row < q_len ? qrow[d] : 0.0f;
         o[d] = 0.0f;
     }
-    const size_t kv_head = ((size_t)b * a.kv_heads + kvh) * (size_t)a.kv_len;
-    const float* kg = (const float*)a.k + kv_head * D;
-    const float* vg = (const float*)a.v + kv_head * D;
+    const float* kg = (const float*)a.k + ir.kv_base;
+    const float* vg = (const float*)a.v + ir.kv_base;
 
     float m_run = kNegInf, l_run = 0.0f;
     const int t_begin = k_begin / kKeys;
@@ -80,8 +80,8 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
             const int j = kbase + r;
             f32x4 kk = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
             if (j < valid) {
-                kk = *(const f32x4*)(kg + (size_t)j * D + 4 * c4);
-                vv = *(const f32x4*)(vg + (size_t)j * D + 4 * c4);
+                kk = *(const f32x4*)(kg + (size_t)j * ir.kv_rs + 4 * c4);
+                vv = *(const f32x4*)(vg + (size_t)j * ir.kv_rs + 4 * c4);
             }
             *(f32x4*)(k_lds + r * D + 4 * c4) = kk;
             *(f32x4*)(v_lds + r * D + 4 * c4) = vv;
@@ -115,9 +115,9 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
         }
     }
 
-    if (row >= a.q_len) return;
+    if (row >= q_len) return;
     const float inv = (hi_r >= 0 && l_run > 0.0f) ? 1.0f / l_run : 0.0f;
-    float* orow = (float*)a.out + (q_head + (size_t)row) * D;
+    float* orow = (float*)a.out + ir.q_base + (size_t)row * ir.q_rs;
 #pragma unroll
     for (int d = 0; d < D; d += 4) *(f32x4*)(orow + d) = f32x4{o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv};
 }

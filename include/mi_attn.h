@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_VERSION 2
+#define MI_ATTN_VERSION 3
 
 typedef enum { MI_ATTN_F32 = 0, MI_ATTN_BF16 = 1 } mi_attn_dtype;
 
@@ -91,6 +91,31 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int bat
                  int kv_heads, int q_len, int kv_len, int head_dim, int pos_offset,
                  const int32_t* seq_lens, int window, int causal, float scale, int dtype,
                  void* stream);
+
+/*
+ * attn_prefill_varlen -- attn_prefill on an unpadded batch: the items' tokens are
+ * concatenated, token-major, with cu_seqlens marking the item boundaries.  Follows
+ * `prepare_batch_unpadded` of the ripvec-core `Driver` page (tokens concatenated flat,
+ * cu_seqlens for the attention boundaries) and reads and writes the [tokens, hidden]
+ * layout directly, where the pages pad around the per-head products and transpose
+ * afterwards (`fused_pad_qkv_split_f16`, `fused_reshape_unpad_f16`; ferrum-kernels
+ * `Backend`, `transpose_head_to_token`).  Keys are the item's own tokens (self-attention,
+ * query i of an item at position i).
+ *
+ *   q, out     [tokens, q_heads,  head_dim]   token-major: row t is token t's hidden vector
+ *   k, v       [tokens, kv_heads, head_dim]
+ *   cu_seqlens DEVICE int32 [batch + 1]: item b is tokens [cu_seqlens[b], cu_seqlens[b+1]).
+ *              Must be non-decreasing from cu_seqlens[0] >= 0, with cu_seqlens[batch] <=
+ *              tokens; an item of length 0 is empty.  The host does not read it.
+ *   max_seqlen the longest item (sizes the launch).  An item longer than that is treated
+ *              as its first max_seqlen tokens; its later rows of out are not written.
+ *   window, causal, scale, dtype as for attn_prefill.  Rows of out between items' tokens
+ *   do not exist: every token row of an item is written.
+ *   batch == 0 or max_seqlen == 0 is a valid empty call.
+ */
+int attn_prefill_varlen(const void* q, const void* k, const void* v, void* out, const int32_t* cu_seqlens,
+                        int batch, int max_seqlen, int q_heads, int kv_heads, int head_dim, int window, int causal,
+                        float scale, int dtype, void* stream);
 
 /*
  * attn_decode -- one query token per (item, query head) against a head-major KV cache.

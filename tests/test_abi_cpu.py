@@ -169,3 +169,33 @@ def test_decode_append_validation(kw, status, msg):
 def test_per_item_empty_batch_is_ok_without_a_gpu():
     assert per_cache(batch=0, kv_lens=None) == mi.MI_ATTN_OK
     assert append(batch=0, k_new=None, v_new=None) == mi.MI_ATTN_OK
+
+
+def varlen(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, cu=FAKE, batch=3, max_seqlen=100, q_heads=8, kv_heads=2,
+                head_dim=64, window=0, causal=0, scale=0.125, dtype=mi.MI_ATTN_BF16, stream=None)
+    args.update(kw)
+    return mi.library().attn_prefill_varlen(*args.values())
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(q_heads=6, kv_heads=4), mi.MI_ATTN_ERR_INVALID, "not a multiple"),
+    (dict(max_seqlen=-1), mi.MI_ATTN_ERR_INVALID, "negative size"),
+    (dict(batch=-2), mi.MI_ATTN_ERR_INVALID, "negative size"),
+    (dict(window=-1), mi.MI_ATTN_ERR_INVALID, "negative"),
+    (dict(scale=-math.inf), mi.MI_ATTN_ERR_INVALID, "not finite"),
+    (dict(head_dim=256), mi.MI_ATTN_ERR_UNSUPPORTED, "head_dim 256"),
+    (dict(dtype=3), mi.MI_ATTN_ERR_UNSUPPORTED, "dtype"),
+    (dict(cu=None), mi.MI_ATTN_ERR_INVALID, "null"),
+    (dict(k=ctypes.c_void_p(0x100002)), mi.MI_ATTN_ERR_INVALID, "aligned"),
+    (dict(cu=ctypes.c_void_p(0x100002)), mi.MI_ATTN_ERR_INVALID, "aligned"),
+])
+def test_prefill_varlen_validation(kw, status, msg):
+    assert varlen(**kw) == status
+    err = mi.attn_last_error()
+    assert err.startswith("attn_prefill_varlen: ") and msg in err
+
+
+def test_prefill_varlen_empty_calls_are_ok_without_a_gpu():
+    assert varlen(batch=0, cu=None) == mi.MI_ATTN_OK
+    assert varlen(max_seqlen=0, q=None) == mi.MI_ATTN_OK

@@ -12,7 +12,8 @@ bits.  Padded positions keep their random values.
 The five named workloads are the shapes the pages' backends run attention on: a tiny
 fp32 causal check, a BERT-base encoder batch with padding, a ModernBERT-style local
 (banded) layer, a causal GQA prefill and a batched GQA decode over a head-major cache.
-A sixth is that decode with the new token's K/V row appended to the cache first.
+Two more are the BERT batch in the unpadded token-major layout and that decode with the
+new token's K/V row appended to the cache first.
 """
 from __future__ import annotations
 
@@ -52,7 +53,7 @@ def draw(rng: np.random.Generator, shape, sigma: float, dtype: str) -> np.ndarra
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "prefill", "decode" or "decode_append"
+    kind: str                 # "prefill", "prefill_varlen", "decode" or "decode_append"
     batch: int
     q_heads: int
     kv_heads: int
@@ -85,6 +86,10 @@ WORKLOADS = {
                                  True, scale=1.0 / math.sqrt(128), seed=4),
     "gqa_decode_kv8192": Workload("gqa_decode_kv8192", "decode", 64, 32, 8, 1, 8192, 128, "bf16", 1.0,
                                   True, pos_offset=8191, capacity=8192, seed=5),
+    # the BERT-shaped batch without padding: the same item lengths, tokens concatenated
+    # token-major ([tokens, heads, head_dim]) with cu_seqlens boundaries
+    "bert_base_varlen": Workload("bert_base_varlen", "prefill_varlen", 32, 12, 12, 512, 512, 64, "bf16", 1.0,
+                                 False, seq_len_range=(16, 512), seed=2),
     # the same decode step with the new token's K/V row appended to each item's cache
     # first: 8191 tokens already cached, the new one goes to slot 8191
     "gqa_decode_append_kv8192": Workload("gqa_decode_append_kv8192", "decode_append", 64, 32, 8, 1, 8192, 128,
@@ -96,6 +101,8 @@ def make_inputs(w: Workload) -> dict:
     """Arrays for a workload, in the draw order of the recipe above.
 
     prefill: q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D], seq_lens [B] int32 or None
+    prefill_varlen: q [T,Hq,D], k/v [T,Hkv,D] token-major over the items' T tokens (drawn
+             after the lengths), seq_lens [B], cu_seqlens [B+1] int32
     decode:  q [B,Hq,D], k/v caches [B,Hkv,capacity,D], kv_lens None
     decode_append: as decode, then the new rows k_new/v_new [B,Hkv,D] (drawn after the
              caches) and cache_lens [B] int32 (the per-item lengths when drawn, else
@@ -106,6 +113,14 @@ def make_inputs(w: Workload) -> dict:
     if w.seq_len_range is not None:
         lo, hi = w.seq_len_range
         seq_lens = rng.integers(lo, hi, endpoint=True, size=w.batch).astype(np.int32)
+    if w.kind == "prefill_varlen":
+        lens = seq_lens if seq_lens is not None else np.full(w.batch, w.q_len, np.int32)
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        T = int(cu[-1])
+        q = draw(rng, (T, w.q_heads, w.head_dim), w.sigma, w.dtype)
+        k = draw(rng, (T, w.kv_heads, w.head_dim), w.sigma, w.dtype)
+        v = draw(rng, (T, w.kv_heads, w.head_dim), w.sigma, w.dtype)
+        return {"q": q, "k": k, "v": v, "seq_lens": lens, "cu_seqlens": cu}
     if w.kind == "prefill":
         q = draw(rng, (w.batch, w.q_heads, w.q_len, w.head_dim), w.sigma, w.dtype)
         k = draw(rng, (w.batch, w.kv_heads, w.kv_len, w.head_dim), w.sigma, w.dtype)
