@@ -5,8 +5,8 @@ against.  Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` 
 ``bench.py`` may import this package.  It shares no code with ``head_attention_02_amd``
 and the GPU library never calls it.
 
-Arrays are numpy.  A float32 array is read as fp32; a uint16 array is read as the raw
-bits of bf16 values.  Every result is float64 and unrounded.
+Arrays are numpy.  A float32 array is read as fp32, a float16 array as fp16; a uint16
+array is read as the raw bits of bf16 values.  Every result is float64 and unrounded.
 """
 from __future__ import annotations
 
@@ -21,7 +21,7 @@ HERE = Path(__file__).resolve().parent
 SOURCE = HERE / "attn_oracle.c"
 LIBRARY = HERE / "liboracle_attn.so"
 
-_F32, _BF16 = 0, 1
+_F32, _BF16, _F16 = 0, 1, 2
 _dbl_p = ctypes.POINTER(ctypes.c_double)
 _i32_p = ctypes.POINTER(ctypes.c_int32)
 
@@ -55,7 +55,9 @@ def _dtype_code(*arrays: np.ndarray) -> int:
         return _F32
     if kinds == {np.dtype(np.uint16)}:
         return _BF16
-    raise TypeError(f"oracle inputs must all be float32 or all bf16 bits (uint16), got {kinds}")
+    if kinds == {np.dtype(np.float16)}:
+        return _F16
+    raise TypeError(f"oracle inputs must all be float32, all float16 or all bf16 bits (uint16), got {kinds}")
 
 
 def _ptr(a: np.ndarray | None, ctype=ctypes.c_void_p):

@@ -49,7 +49,7 @@
  *   the query sits at pos_offset and sees keys j < kv_len, j <= pos_offset.
  *
  * Inputs are read exactly: fp32 values as stored, bf16 values widened bit-exactly
- * (a bf16 is the upper 16 bits of an fp32).  All arithmetic is in double; the output
+ * (a bf16 is the upper 16 bits of an fp32), fp16 values decoded from their fields.  All arithmetic is in double; the output
  * is double and is never rounded.
  */
 #include <math.h>
@@ -61,12 +61,31 @@
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+#define ORACLE_F16 2
 
-/* Read element `idx` of a tensor stored as fp32 or bf16, widened to double. */
+/* IEEE 754 binary16 bits -> double, from the format's definition: sign bit 15, biased
+ * exponent bits 14..10 (bias 15), fraction bits 9..0; exponent 0 is subnormal
+ * (fraction * 2^-24), exponent 31 is infinity (fraction 0) or NaN. */
+static double half_to_double(uint16_t h) {
+    const int sign = (h >> 15) & 1;
+    const int expo = (h >> 10) & 0x1f;
+    const int frac = h & 0x3ff;
+    double mag;
+    if (expo == 0)
+        mag = ldexp((double)frac, -24);
+    else if (expo == 31)
+        mag = frac == 0 ? INFINITY : NAN;
+    else
+        mag = ldexp(1024.0 + frac, expo - 25);
+    return sign ? -mag : mag;
+}
+
+/* Read element `idx` of a tensor stored as fp32, bf16 or fp16, widened to double. */
 static double load_elem(const void* base, int dtype, int64_t idx) {
     if (dtype == ORACLE_F32) {
         return (double)((const float*)base)[idx];
     }
+    if (dtype == ORACLE_F16) return half_to_double(((const uint16_t*)base)[idx]);
     uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
@@ -263,7 +282,7 @@ static int check_shape(const problem_t* P) {
         P->head_dim < 1 || P->window < 0)
         return -1;
     if (P->q_heads % P->kv_heads != 0) return -1;
-    if (P->dtype != ORACLE_F32 && P->dtype != ORACLE_BF16) return -1;
+    if (P->dtype != ORACLE_F32 && P->dtype != ORACLE_BF16 && P->dtype != ORACLE_F16) return -1;
     if (P->kv_stride < P->kv_len) return -1;
     return 0;
 }

@@ -569,4 +569,33 @@ def pin_varlen_item_order(oracle):
         _close(a[4, h], _f64(v[4, h // 2]), 0.0, "single-token item")
 
 
+# ---------------------------------------------------------------------------
+# fp16 inputs (ripvec-core `Driver`, the `_f16` twins: half storage)
+
+def pin_f16_every_value_exact(oracle):
+    """Every fp16 bit pattern is read exactly: with one key, out = that key's V row, so a
+    V row holding all 63488 finite fp16 values must come back as numpy's widening of
+    them; the infinities and a NaN come back as themselves."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = bits[(bits & 0x7C00) != 0x7C00]
+    special = np.array([0x7C00, 0xFC00, 0x7E00], np.uint16)   # +inf, -inf, NaN
+    for vals in (finite, special):
+        n = vals.size
+        v = vals.view(np.float16).reshape(1, 1, 1, n)
+        z = np.zeros((1, 1, 1, n), np.float16)
+        out = oracle.prefill(z, z, v, scale=1.0)
+        want = vals.view(np.float16).astype(np.float64)
+        assert np.array_equal(out[0, 0, 0], want, equal_nan=True), "fp16 decode"
+
+
+def pin_f16_widening(oracle):
+    """fp16 inputs equal their exact fp32 widening (numpy's conversion)."""
+    rng = _rng(414)
+    x = rng.standard_normal((3, 2, 4, 9, 8), dtype=np.float32).astype(np.float16)
+    a = oracle.prefill(x[0], x[1][:, :2], x[2][:, :2], scale=0.5, causal=True, window=5)
+    w = x.astype(np.float32)
+    b = oracle.prefill(w[0], w[1][:, :2], w[2][:, :2], scale=0.5, causal=True, window=5)
+    _close(a, b, 0.0, "fp16 vs widened fp32")
+
+
 PINS = {name[4:]: fn for name, fn in sorted(globals().items()) if name.startswith("pin_") and callable(fn)}

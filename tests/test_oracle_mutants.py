@@ -32,6 +32,9 @@ MUTANTS = {
                              "(((int64_t)b * P->q_heads + kh) * P->q_len + i) * D"),
     "last_dim_dropped": ("for (int d = 0; d < D; ++d)\n            dot +=",
                          "for (int d = 0; d < D - 1; ++d)\n            dot +="),
+    "f16_exponent_bias": ("ldexp(1024.0 + frac, expo - 25)", "ldexp(1024.0 + frac, expo - 24)"),
+    "f16_subnormal_scale": ("ldexp((double)frac, -24)", "ldexp((double)frac, -23)"),
+    "f16_sign_dropped": ("return sign ? -mag : mag;", "return mag;"),
     "bf16_low_half": ("uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;",
                       "uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 15;"),
 }
