@@ -35,7 +35,7 @@ sys.path.insert(0, str(ROOT))
 
 import workloads as W  # noqa: E402
 
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 (and fp16) MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (vector)
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 PROFILES = ROOT / "profiles"
@@ -73,7 +73,7 @@ def prefill_flops(w: W.Workload, seq_lens) -> float:
 
 def prefill_bytes(w: W.Workload, seq_lens) -> float:
     """Q + valid K/V rows + O, each once."""
-    esz = 2 if w.dtype == "bf16" else 4
+    esz = 4 if w.dtype == "f32" else 2
     if w.kind == "prefill_varlen":   # every token row is an item's
         return 2.0 * (w.q_heads + w.kv_heads) * w.head_dim * esz * float(np.sum(seq_lens))
     valid = np.full(w.batch, w.kv_len) if seq_lens is None else np.clip(seq_lens, 0, w.kv_len)
@@ -83,7 +83,7 @@ def prefill_bytes(w: W.Workload, seq_lens) -> float:
 
 
 def decode_bytes(w: W.Workload) -> float:
-    esz = 2 if w.dtype == "bf16" else 4
+    esz = 4 if w.dtype == "f32" else 2
     keys = min(w.pos_offset + 1, w.kv_len)
     kv = 2.0 * w.batch * w.kv_heads * keys * w.head_dim * esz
     qo = 2.0 * w.batch * w.q_heads * w.head_dim * esz
@@ -242,7 +242,7 @@ def cpu_baseline_decode(w: W.Workload, x: dict, budget_s: float) -> dict:
         if dt >= budget_s / 4 or n == total:
             break
         n = min(total, max(n * 2, int(n * budget_s / max(dt, 1e-3))))
-    esz = 2 if w.dtype == "bf16" else 4
+    esz = 4 if w.dtype == "f32" else 2
     # bytes of K and V each query row streams (the GPU reads each once per KV head group)
     by = 2.0 * n * min(w.pos_offset + 1, w.kv_len) * w.head_dim * esz
     return {"value": by / dt / 1e9, "unit": "GB/s", "cores": ref.threads_used, "kind": "oracle",
@@ -414,8 +414,8 @@ def main() -> int:
         sec = ms / 1e3
         if w.kind in ("prefill", "prefill_varlen"):
             fl = prefill_flops(w, x["seq_lens"])
-            peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-            if w.dtype != "bf16":
+            peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS   # fp16 dense = bf16 dense
+            if w.dtype == "f32":
                 src = ["prefill_f32.hip", "mi_attn_device.hpp"]
             elif w.head_dim == 128:
                 src = ["prefill_bf16.hip", "mi_attn_device.hpp"]

@@ -33,7 +33,7 @@ from pathlib import Path
 
 LIBRARY = Path(__file__).resolve().parent / "libmi_attn.so"
 
-MI_ATTN_F32, MI_ATTN_BF16 = 0, 1
+MI_ATTN_F32, MI_ATTN_BF16, MI_ATTN_F16 = 0, 1, 2
 MI_ATTN_OK, MI_ATTN_ERR_INVALID, MI_ATTN_ERR_UNSUPPORTED, MI_ATTN_ERR_HIP = 0, 1, 2, 3
 
 EXPORTS = ("attn_prefill", "attn_prefill_varlen", "attn_decode", "attn_decode_per_cache", "attn_decode_append",
@@ -105,7 +105,9 @@ def _dtype_code(t) -> int:
         return MI_ATTN_BF16
     if t.dtype == torch.float32:
         return MI_ATTN_F32
-    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+    if t.dtype == torch.float16:
+        return MI_ATTN_F16
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16, float16 or float32)")
 
 
 def _dev(t, name: str, dtype=None):

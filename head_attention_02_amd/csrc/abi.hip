@@ -39,7 +39,7 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int bat
                  void* stream) {
     g_error[0] = '\0';
     const char* fn = "attn_prefill";
-    if (dtype != MI_ATTN_BF16 && dtype != MI_ATTN_F32)
+    if (dtype != MI_ATTN_BF16 && dtype != MI_ATTN_F32 && dtype != MI_ATTN_F16)
         return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
     if (batch < 0 || q_len < 0 || kv_len < 0)
         return fail(MI_ATTN_ERR_INVALID, "%s: negative size (batch %d, q_len %d, kv_len %d)", fn, batch,
@@ -82,8 +82,9 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int bat
     a.causal = causal ? 1 : 0;
     a.scale = scale;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = dtype == MI_ATTN_BF16 ? mi_attn::launch_prefill_bf16(a, head_dim, s)
-                                         : mi_attn::launch_prefill_f32(a, head_dim, s);
+    a.f16 = dtype == MI_ATTN_F16;
+    hipError_t e = dtype != MI_ATTN_F32 ? mi_attn::launch_prefill_bf16(a, head_dim, s)
+                                        : mi_attn::launch_prefill_f32(a, head_dim, s);
     if (e != hipSuccess) return fail(MI_ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return MI_ATTN_OK;
 }
@@ -93,7 +94,7 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v, void* out, 
                         float scale, int dtype, void* stream) {
     g_error[0] = '\0';
     const char* fn = "attn_prefill_varlen";
-    if (dtype != MI_ATTN_BF16 && dtype != MI_ATTN_F32)
+    if (dtype != MI_ATTN_BF16 && dtype != MI_ATTN_F32 && dtype != MI_ATTN_F16)
         return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
     if (batch < 0 || max_seqlen < 0)
         return fail(MI_ATTN_ERR_INVALID, "%s: negative size (batch %d, max_seqlen %d)", fn, batch, max_seqlen);
@@ -131,8 +132,9 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v, void* out, 
     a.causal = causal ? 1 : 0;
     a.scale = scale;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = dtype == MI_ATTN_BF16 ? mi_attn::launch_prefill_bf16(a, head_dim, s)
-                                         : mi_attn::launch_prefill_f32(a, head_dim, s);
+    a.f16 = dtype == MI_ATTN_F16;
+    hipError_t e = dtype != MI_ATTN_F32 ? mi_attn::launch_prefill_bf16(a, head_dim, s)
+                                        : mi_attn::launch_prefill_f32(a, head_dim, s);
     if (e != hipSuccess) return fail(MI_ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return MI_ATTN_OK;
 }
@@ -152,7 +154,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o
                 size_t workspace_bytes, void* stream) {
     g_error[0] = '\0';
     const char* fn = "attn_decode";
-    if (dtype != MI_ATTN_BF16 && dtype != MI_ATTN_F32)
+    if (dtype != MI_ATTN_BF16 && dtype != MI_ATTN_F32 && dtype != MI_ATTN_F16)
         return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
     if (batch < 0) return fail(MI_ATTN_ERR_INVALID, "%s: negative batch (%d)", fn, batch);
     if (q_heads < 1 || kv_heads < 1)
@@ -203,7 +205,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o
     a.splits = p.splits;
     a.split_len = p.split_len;
     a.head_groups = p.head_groups;
-    hipError_t e = mi_attn::launch_decode(a, head_dim, p.heads_per_group, dtype == MI_ATTN_BF16,
+    hipError_t e = mi_attn::launch_decode(a, head_dim, p.heads_per_group, dtype,
                                           (hipStream_t)stream);
     if (e != hipSuccess) return fail(MI_ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return MI_ATTN_OK;
@@ -219,7 +221,7 @@ int decode_per_item(const char* fn, const void* q, const void* const* k_caches, 
                     int capacity, int head_dim, const int32_t* lens, int window, float scale, int dtype,
                     void* workspace, size_t workspace_bytes, void* stream) {
     g_error[0] = '\0';
-    if (dtype != MI_ATTN_BF16 && dtype != MI_ATTN_F32)
+    if (dtype != MI_ATTN_BF16 && dtype != MI_ATTN_F32 && dtype != MI_ATTN_F16)
         return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
     if (batch < 0) return fail(MI_ATTN_ERR_INVALID, "%s: negative batch (%d)", fn, batch);
     if (q_heads < 1 || kv_heads < 1)
@@ -270,7 +272,7 @@ int decode_per_item(const char* fn, const void* q, const void* const* k_caches, 
     a.splits = p.splits;
     a.split_len = p.split_len;
     a.head_groups = p.head_groups;
-    hipError_t e = mi_attn::launch_decode(a, head_dim, p.heads_per_group, dtype == MI_ATTN_BF16,
+    hipError_t e = mi_attn::launch_decode(a, head_dim, p.heads_per_group, dtype,
                                           (hipStream_t)stream);
     if (e != hipSuccess) return fail(MI_ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return MI_ATTN_OK;

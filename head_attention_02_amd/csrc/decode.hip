@@ -19,6 +19,8 @@
 // splits are merged exactly: m* = max m_s, out = sum_s 2^(m_s - m*) o_s / sum_s 2^(m_s - m*) l_s.
 // With a single split (enough (item, kv head) units to fill the GPU) the first pass
 // normalises and stores the output itself, and there is no workspace and no second pass.
+#include <type_traits>
+
 #include "mi_attn_device.hpp"
 #include "mi_attn_kernels.hpp"
 
@@ -33,15 +35,18 @@ constexpr int kSteps = 8;   // wave loads per batch (rows per lane group between
 // exactly once: it is issued non-temporal, so the rows stream through the caches without
 // displacing anything (a plain-load read of 2 GiB measured about 6.3 TB/s on MI355X, the
 // same read with non-temporal loads about 7.0 TB/s).
-template <bool BF16, bool STREAM = false>
+// Element formats (the values of mi_attn_dtype).
+constexpr int kF32 = 0, kBF16 = 1, kF16 = 2;
+
+template <int FMT, bool STREAM = false>
 __device__ __forceinline__ void load8(const void* base, size_t elem, float* x) {
-    if constexpr (BF16) {
+    if constexpr (FMT != kF32) {
         const u32x4* src = (const u32x4*)((const uint16_t*)base + elem);
         const u32x4 w = STREAM ? __builtin_nontemporal_load(src) : *src;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            x[2 * i] = bf16_lo(w[i]);
-            x[2 * i + 1] = bf16_hi(w[i]);
+            x[2 * i] = FMT == kBF16 ? bf16_lo(w[i]) : f16_lo(w[i]);
+            x[2 * i + 1] = FMT == kBF16 ? bf16_hi(w[i]) : f16_hi(w[i]);
         }
     } else {
         const f32x4* src = (const f32x4*)((const float*)base + elem);
@@ -55,14 +60,14 @@ __device__ __forceinline__ void load8(const void* base, size_t elem, float* x) {
     }
 }
 
-// The 16 (bf16) or 32 (fp32) bytes of eight consecutive elements, copied unchanged.
-template <bool BF16>
+// The 16 (bf16, fp16) or 32 (fp32) bytes of eight consecutive elements, copied unchanged.
+template <int FMT>
 __device__ __forceinline__ void copy8(const void* src, size_t src_elem, void* dst, size_t dst_elem) {
-    constexpr int esz = BF16 ? 2 : 4;
+    constexpr int esz = FMT == kF32 ? 4 : 2;
     const u32x4* s = (const u32x4*)((const char*)src + src_elem * esz);
     u32x4* d = (u32x4*)((char*)dst + dst_elem * esz);
     d[0] = s[0];
-    if constexpr (!BF16) d[1] = s[1];
+    if constexpr (FMT == kF32) d[1] = s[1];
 }
 
 // Cache addressing modes of the split kernel.
@@ -72,7 +77,18 @@ enum CacheMode {
     kAppend = 2,    // per item, and the new token's K/V row is appended before attending
 };
 
-template <int D, int GT, bool BF16, int MODE>
+// One result in the output format (round to nearest even for the 16-bit formats).
+template <int FMT>
+__device__ __forceinline__ void store1(void* out, size_t at, float v) {
+    if constexpr (FMT == kBF16)
+        ((__bf16*)out)[at] = (__bf16)v;
+    else if constexpr (FMT == kF16)
+        ((_Float16*)out)[at] = (_Float16)v;
+    else
+        ((float*)out)[at] = v;
+}
+
+template <int D, int GT, int FMT, int MODE>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     constexpr int LPR = D / 8;            // lanes per key row, 8 elements per lane
     constexpr int RPW = 64 / LPR;         // rows per wave load
@@ -120,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     float qf[GT][8];
 #pragma unroll
     for (int t = 0; t < GT; ++t) {
-        load8<BF16>(a.q, ((size_t)b * a.q_heads + h0 + t) * D + c * 8, qf[t]);
+        load8<FMT>(a.q, ((size_t)b * a.q_heads + h0 + t) * D + c * 8, qf[t]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) qf[t][i] *= c2;
     }
@@ -149,8 +165,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     const size_t new_row = ((size_t)b * a.kv_heads + kvh) * D + c * 8;
     if constexpr (MODE == kAppend) {
         if (hg == 0 && pos >= s0 && pos < s1 && tid < LPR) {
-            copy8<BF16>(a.k_new, new_row, (void*)kc, head_base + (size_t)pos * D + c * 8);
-            copy8<BF16>(a.v_new, new_row, (void*)vc, head_base + (size_t)pos * D + c * 8);
+            copy8<FMT>(a.k_new, new_row, (void*)kc, head_base + (size_t)pos * D + c * 8);
+            copy8<FMT>(a.v_new, new_row, (void*)vc, head_base + (size_t)pos * D + c * 8);
         }
     }
     for (int base = s0; base < s1; base += BATCH) {
@@ -162,9 +178,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
             const int kr = key[u] < s1 ? key[u] : s0;     // out-of-range rows read a valid row
             if constexpr (MODE == kAppend) {
                 const bool nw = kr == pos;
-                load8<BF16, true>(nw ? a.k_new : kc, nw ? new_row : head_base + (size_t)kr * D + c * 8, kx[u]);
+                load8<FMT, true>(nw ? a.k_new : kc, nw ? new_row : head_base + (size_t)kr * D + c * 8, kx[u]);
             } else {
-                load8<BF16, true>(kc, head_base + (size_t)kr * D + c * 8, kx[u]);
+                load8<FMT, true>(kc, head_base + (size_t)kr * D + c * 8, kx[u]);
             }
         }
         float s[kSteps][GT];
@@ -185,9 +201,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
             const int kr = key[u] < s1 ? key[u] : s0;
             if constexpr (MODE == kAppend) {
                 const bool nw = kr == pos;
-                load8<BF16, true>(nw ? a.v_new : vc, nw ? new_row : head_base + (size_t)kr * D + c * 8, vx[u]);
+                load8<FMT, true>(nw ? a.v_new : vc, nw ? new_row : head_base + (size_t)kr * D + c * 8, vx[u]);
             } else {
-                load8<BF16, true>(vc, head_base + (size_t)kr * D + c * 8, vx[u]);
+                load8<FMT, true>(vc, head_base + (size_t)kr * D + c * 8, vx[u]);
             }
         }
 #pragma unroll
@@ -242,11 +258,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
             // combine pass would compute from this one partial state, bit for bit)
             const size_t at = ((size_t)b * a.q_heads + h0 + t) * D + d;
             const float res = ll > 0.0f ? acc / ll : 0.0f;
-            if constexpr (BF16) {
-                ((__bf16*)a.out)[at] = (__bf16)res;
-            } else {
-                ((float*)a.out)[at] = res;
-            }
+            store1<FMT>(a.out, at, res);
         } else {
             float* ws = a.ws + (((size_t)b * a.q_heads + h0 + t) * a.splits + split) * (D + 2);
             ws[d] = acc;
@@ -258,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     }
 }
 
-template <int D, bool BF16>
+template <int D, int FMT>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
     const int d = threadIdx.x;
     const size_t bh = blockIdx.x;   // b * q_heads + h
@@ -273,37 +285,33 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
         ll = fmaf(w, ws[s * (D + 2) + D + 1], ll);
     }
     const float res = ll > 0.0f ? acc / ll : 0.0f;
-    if constexpr (BF16) {
-        ((__bf16*)a.out)[bh * D + d] = (__bf16)res;
-    } else {
-        ((float*)a.out)[bh * D + d] = res;
-    }
+    store1<FMT>(a.out, bh * D + d, res);
 }
 
-template <int D, bool BF16, int MODE>
+template <int D, int FMT, int MODE>
 void launch_split(const DecodeArgs& a, int gt, dim3 grid, hipStream_t stream) {
     const dim3 block(kThreads);
     switch (gt) {
-        case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1, BF16, MODE>), grid, block, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, BF16, MODE>), grid, block, 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((decode_split_kernel<D, 4, BF16, MODE>), grid, block, 0, stream, a); break;
-        case 8: hipLaunchKernelGGL((decode_split_kernel<D, 8, BF16, MODE>), grid, block, 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1, FMT, MODE>), grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, FMT, MODE>), grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((decode_split_kernel<D, 4, FMT, MODE>), grid, block, 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((decode_split_kernel<D, 8, FMT, MODE>), grid, block, 0, stream, a); break;
     }
 }
 
-template <int D, bool BF16>
+template <int D, int FMT>
 hipError_t launch_d(const DecodeArgs& a, int gt, hipStream_t stream) {
     if (gt != 1 && gt != 2 && gt != 4 && gt != 8) return hipErrorInvalidValue;
     const dim3 grid(a.splits, a.kv_heads * a.head_groups, a.batch);
     if (a.k_new)
-        launch_split<D, BF16, kAppend>(a, gt, grid, stream);
+        launch_split<D, FMT, kAppend>(a, gt, grid, stream);
     else if (a.k_ptrs)
-        launch_split<D, BF16, kPerItem>(a, gt, grid, stream);
+        launch_split<D, FMT, kPerItem>(a, gt, grid, stream);
     else
-        launch_split<D, BF16, kStacked>(a, gt, grid, stream);
+        launch_split<D, FMT, kStacked>(a, gt, grid, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<D, BF16>), dim3(a.batch * a.q_heads), dim3(D), 0, stream, a);
+    hipLaunchKernelGGL((decode_combine_kernel<D, FMT>), dim3(a.batch * a.q_heads), dim3(D), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -333,12 +341,22 @@ DecodePlan plan_decode(int batch, int q_heads, int kv_heads, int kv_len, int hea
     return p;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int head_dim, int heads_per_group, bool bf16,
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, int heads_per_group, int dtype,
                          hipStream_t stream) {
+    const int gt = heads_per_group;
+    auto by_format = [&](auto d_c) -> hipError_t {
+        constexpr int D = decltype(d_c)::value;
+        switch (dtype) {
+            case kF32: return launch_d<D, kF32>(a, gt, stream);
+            case kBF16: return launch_d<D, kBF16>(a, gt, stream);
+            case kF16: return launch_d<D, kF16>(a, gt, stream);
+            default: return hipErrorInvalidValue;
+        }
+    };
     switch (head_dim) {
-        case 32: return bf16 ? launch_d<32, true>(a, heads_per_group, stream) : launch_d<32, false>(a, heads_per_group, stream);
-        case 64: return bf16 ? launch_d<64, true>(a, heads_per_group, stream) : launch_d<64, false>(a, heads_per_group, stream);
-        case 128: return bf16 ? launch_d<128, true>(a, heads_per_group, stream) : launch_d<128, false>(a, heads_per_group, stream);
+        case 32: return by_format(std::integral_constant<int, 32>{});
+        case 64: return by_format(std::integral_constant<int, 64>{});
+        case 128: return by_format(std::integral_constant<int, 128>{});
         default: return hipErrorInvalidValue;
     }
 }

@@ -30,6 +30,41 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, p);
 }
 
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+
+// fp16 bits -> fp32 (exact widening).
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// Two fp32 -> packed fp16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+    f16x2 p;
+    p[0] = (_Float16)lo;
+    p[1] = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+// The two 16-bit input formats of the matrix-core kernels.  Operands are handled as
+// eight raw 16-bit values (bf16x8 bit patterns); Fmt16<F16> picks the MFMA that reads
+// them and the rounding of fp32 results back to the format.
+template <bool F16>
+struct Fmt16 {
+    __device__ static __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+        if constexpr (F16)
+            return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                          c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
+        if constexpr (F16)
+            return pack_f16x2(lo, hi);
+        else
+            return pack_bf16x2(lo, hi);
+    }
+};
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Sum / max over the 16 lanes of a DPP row, result in every lane of the row.

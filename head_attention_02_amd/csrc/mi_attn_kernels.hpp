@@ -23,6 +23,7 @@ struct PrefillArgs {
     int pos_offset, window, causal;
     float scale;
     int n_qtiles;             // grid.x
+    int f16;                  // 16-bit inputs: 0 = bf16, 1 = fp16 (matrix-core kernels)
 };
 
 // Where one (item, query head)'s rows live and how many there are (element offsets and
@@ -86,7 +87,8 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, hipStream_t s
 // head dims 32 and 64 (called by launch_prefill_bf16)
 hipError_t launch_prefill_bf16_narrow(const PrefillArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs& a, int head_dim, int heads_per_group, bool bf16,
+// dtype: an mi_attn_dtype value (the element format of q, the caches and out)
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, int heads_per_group, int dtype,
                          hipStream_t stream);
 
 // Decode launch plan shared by the call and the workspace query.

@@ -1,5 +1,6 @@
-// prefill_bf16.hip -- fused attention prefill for bf16 inputs on gfx950 matrix cores
-// (head dim 128; head dims 32 and 64 run prefill_bf16_narrow.hip).
+// prefill_bf16.hip -- fused attention prefill for 16-bit inputs (bf16, and fp16 through
+// the same code with the fp16 MFMA) on gfx950 matrix cores (head dim 128; head dims 32
+// and 64 run prefill_bf16_narrow.hip).
 //
 // Computes softmax(scale * Q K^T + mask) V per (item, query head) in one pass over the
 // keys, without materialising the score matrix: the scores of one key tile live in
@@ -112,9 +113,10 @@ __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70);
 // keeps it a branch instead of computing its body on every tile and selecting.
 __device__ __forceinline__ void keep_branch() { asm volatile("" ::); }
 
-template <int D, bool POS_SCALE>
+template <int D, bool POS_SCALE, bool F16>
 struct Prefill {
     using G = Geo<D>;
+    using H = Fmt16<F16>;
 
     // ---- per-lane constants ---------------------------------------------------------
     int lane, wave, g;
@@ -241,7 +243,7 @@ struct Prefill {
                 const int kb2 = f % 2, kc = f / 2;
                 const bf16x8 k_now = kf[f % PF];
                 if (f + PF < NF) kf[f % PF] = k_frag(kbuf, blk(f + PF));
-                s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_now, qf[kc], kc == 0 ? f32x16{} : s[kb2], 0, 0, 0);
+                s[kb2] = H::mfma32x32x16(k_now, qf[kc], kc == 0 ? f32x16{} : s[kb2]);
                 __builtin_amdgcn_sched_barrier(0);   // keep the reads PF steps ahead, no further
             }
         }
@@ -255,7 +257,7 @@ struct Prefill {
                 const int c4 = j / G::DB, db = j % G::DB;
                 const bf16x8 v_now = vf[j % PF];
                 if (j + PF < NJ) vf[j % PF] = v_frag(vbuf, j + PF);
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_now, pf[c4], o[db], 0, 0, 0);
+                o[db] = H::mfma32x32x16(v_now, pf[c4], o[db]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -323,7 +325,7 @@ struct Prefill {
                 const float s0 = s[c4 / 2][8 * (c4 % 2) + jj], s1 = s[c4 / 2][8 * (c4 % 2) + jj + 1];
                 const float p0 = POS_SCALE ? fast_exp2(fmaf(s0, c2, -m_use)) : fast_exp2(s0 - m_use);
                 const float p1 = POS_SCALE ? fast_exp2(fmaf(s1, c2, -m_use)) : fast_exp2(s1 - m_use);
-                w[jj / 2] = pack_bf16x2(p0, p1);
+                w[jj / 2] = H::pack2(p0, p1);
                 ls0 += p0;
                 ls1 += p1;
             }
@@ -334,13 +336,14 @@ struct Prefill {
     }
 };
 
-template <int D, bool POS_SCALE>
+template <int D, bool POS_SCALE, bool F16>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a) {
     using G = Geo<D>;
     __shared__ __attribute__((aligned(16))) u32x4 k_lds[2][kBN * G::CPR];
     __shared__ __attribute__((aligned(16))) u32x4 v_lds[2][kBN * G::CPR];
 
-    Prefill<D, POS_SCALE> st;
+    Prefill<D, POS_SCALE, F16> st;
+    using H = Fmt16<F16>;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -551,7 +554,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
         }
     }
 
-    // ---- epilogue: normalise, zero padded / empty rows, store bf16 --------------------
+    // ---- epilogue: normalise, zero padded / empty rows, store in the input format -----
     const float l_tot = halves_sum(st.l_run);
     if (my_row >= q_len) return;
     const float inv = (st.hi_r >= 0 && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
@@ -562,8 +565,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
         for (int e4 = 0; e4 < 4; ++e4) {
             const int d = 32 * db + 8 * e4 + 4 * g;
             u32x2 w;
-            w[0] = pack_bf16x2(st.o[db][4 * e4] * inv, st.o[db][4 * e4 + 1] * inv);
-            w[1] = pack_bf16x2(st.o[db][4 * e4 + 2] * inv, st.o[db][4 * e4 + 3] * inv);
+            w[0] = H::pack2(st.o[db][4 * e4] * inv, st.o[db][4 * e4 + 1] * inv);
+            w[1] = H::pack2(st.o[db][4 * e4 + 2] * inv, st.o[db][4 * e4 + 3] * inv);
             *(u32x2*)(orow + d) = w;
         }
     }
@@ -574,10 +577,18 @@ hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
     PrefillArgs args = a;
     args.n_qtiles = (a.q_len + kBM - 1) / kBM;
     const dim3 grid((unsigned)args.n_qtiles * a.q_heads * a.batch);
-    if (args.scale > 0.0f)
-        hipLaunchKernelGGL((prefill_bf16_kernel<D, true>), grid, dim3(kThreads), 0, stream, args);
-    else
-        hipLaunchKernelGGL((prefill_bf16_kernel<D, false>), grid, dim3(kThreads), 0, stream, args);
+    const dim3 block(kThreads);
+    if (args.f16) {
+        if (args.scale > 0.0f)
+            hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true>), grid, block, 0, stream, args);
+        else
+            hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true>), grid, block, 0, stream, args);
+    } else {
+        if (args.scale > 0.0f)
+            hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false>), grid, block, 0, stream, args);
+        else
+            hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false>), grid, block, 0, stream, args);
+    }
     return hipGetLastError();
 }
 

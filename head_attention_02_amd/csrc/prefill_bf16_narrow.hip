@@ -106,9 +106,10 @@ __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70);
 // keeps it a branch instead of computing its body on every tile and selecting.
 __device__ __forceinline__ void keep_branch() { asm volatile("" ::); }
 
-template <int D, int RB, int W, bool POS_SCALE>
+template <int D, int RB, int W, bool POS_SCALE, bool F16>
 struct Prefill {
     using G = Geo<D, W>;
+    using H = Fmt16<F16>;
 
     // ---- per-lane constants ---------------------------------------------------------
     int lane, wave, g;
@@ -205,7 +206,7 @@ struct Prefill {
             const float s0 = s[rb][c4 / 2][8 * (c4 % 2) + jj], s1 = s[rb][c4 / 2][8 * (c4 % 2) + jj + 1];
             const float p0 = POS_SCALE ? fast_exp2(fmaf(s0, c2, -m_use[rb])) : fast_exp2(s0 - m_use[rb]);
             const float p1 = POS_SCALE ? fast_exp2(fmaf(s1, c2, -m_use[rb])) : fast_exp2(s1 - m_use[rb]);
-            w[jj / 2] = pack_bf16x2(p0, p1);
+            w[jj / 2] = H::pack2(p0, p1);
             ls[rb][0] += p0;
             ls[rb][1] += p1;
         }
@@ -224,7 +225,7 @@ struct Prefill {
             const bf16x8 kf = k_frag(kbuf, f);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-                s[rb][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[rb][kc], kc == 0 ? f32x16{} : s[rb][kb2], 0, 0, 0);
+                s[rb][kb2] = H::mfma32x32x16(kf, qf[rb][kc], kc == 0 ? f32x16{} : s[rb][kb2]);
         }
     }
 
@@ -276,7 +277,7 @@ struct Prefill {
                 if (f + PF < NF) kf[f % PF] = k_frag(kbuf, f + PF);
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
-                    nxt[rb][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_now, qf[rb][kc], kc == 0 ? f32x16{} : nxt[rb][kb2], 0, 0, 0);
+                    nxt[rb][kb2] = H::mfma32x32x16(k_now, qf[rb][kc], kc == 0 ? f32x16{} : nxt[rb][kb2]);
 #pragma unroll
                 for (int u = f * NU / NF; u < (f + 1) * NU / NF; ++u) probs_chunk(cur, pf, ls, m_use, u);
                 __builtin_amdgcn_sched_barrier(0);
@@ -373,7 +374,7 @@ struct Prefill {
             if (j + PF < NJ) vf[j % PF] = v_frag(vbuf, j + PF);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-                o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_now, pf[rb][c4], o[rb][db], 0, 0, 0);
+                o[rb][db] = H::mfma32x32x16(v_now, pf[rb][c4], o[rb][db]);
             if constexpr (HAS_NEXT) {
 #pragma unroll
                 for (int q = j * NP / NJ; q < (j + 1) * NP / NJ; ++q) {
@@ -403,7 +404,7 @@ struct Cfg {
 // launches have such tiles; the full bidirectional launch keeps the ungated stream, whose
 // schedule the extra branches would only disturb (measured 39.9 vs 41.3 us on the padded
 // BERT batch).
-template <int D, bool POS_SCALE, bool GATE>
+template <int D, bool POS_SCALE, bool GATE, bool F16>
 __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_narrow_kernel(PrefillArgs a) {
     constexpr int RB = Cfg<D>::RB;
     constexpr int W = Cfg<D>::W;
@@ -412,7 +413,8 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
     __shared__ __attribute__((aligned(16))) u32x4 k_lds[2][kBN * G::KS];
     __shared__ __attribute__((aligned(16))) u32x4 v_lds[2][kBN * G::CPR];
 
-    Prefill<D, RB, W, POS_SCALE> st;
+    Prefill<D, RB, W, POS_SCALE, F16> st;
+    using H = Fmt16<F16>;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -665,8 +667,8 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
                 for (int e4 = 0; e4 < 4; ++e4) {
                     const int d = 32 * db + 8 * e4 + 4 * g;
                     u32x2 w;
-                    w[0] = pack_bf16x2(st.o[rb][db][4 * e4] * inv, st.o[rb][db][4 * e4 + 1] * inv);
-                    w[1] = pack_bf16x2(st.o[rb][db][4 * e4 + 2] * inv, st.o[rb][db][4 * e4 + 3] * inv);
+                    w[0] = H::pack2(st.o[rb][db][4 * e4] * inv, st.o[rb][db][4 * e4 + 1] * inv);
+                    w[1] = H::pack2(st.o[rb][db][4 * e4 + 2] * inv, st.o[rb][db][4 * e4 + 3] * inv);
                     *(u32x2*)(orow + d) = w;
                 }
             }
@@ -681,13 +683,24 @@ hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)args.n_qtiles * a.q_heads * a.batch);
     const dim3 block(Cfg<D>::THREADS);
     const bool gate = a.causal || a.window > 0;
-    if (args.scale > 0.0f) {
-        if (gate)
-            hipLaunchKernelGGL((prefill_bf16_narrow_kernel<D, true, true>), grid, block, 0, stream, args);
-        else
-            hipLaunchKernelGGL((prefill_bf16_narrow_kernel<D, true, false>), grid, block, 0, stream, args);
+    if (args.f16) {
+        if (args.scale > 0.0f) {
+            if (gate)
+                hipLaunchKernelGGL((prefill_bf16_narrow_kernel<D, true, true, true>), grid, block, 0, stream, args);
+            else
+                hipLaunchKernelGGL((prefill_bf16_narrow_kernel<D, true, false, true>), grid, block, 0, stream, args);
+        } else {
+            hipLaunchKernelGGL((prefill_bf16_narrow_kernel<D, false, true, true>), grid, block, 0, stream, args);
+        }
     } else {
-        hipLaunchKernelGGL((prefill_bf16_narrow_kernel<D, false, true>), grid, block, 0, stream, args);
+        if (args.scale > 0.0f) {
+            if (gate)
+                hipLaunchKernelGGL((prefill_bf16_narrow_kernel<D, true, true, false>), grid, block, 0, stream, args);
+            else
+                hipLaunchKernelGGL((prefill_bf16_narrow_kernel<D, true, false, false>), grid, block, 0, stream, args);
+        } else {
+            hipLaunchKernelGGL((prefill_bf16_narrow_kernel<D, false, true, false>), grid, block, 0, stream, args);
+        }
     }
     return hipGetLastError();
 }

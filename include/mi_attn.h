@@ -33,9 +33,12 @@
  *   - All tensor pointers are DEVICE pointers to contiguous row-major arrays, 16-byte
  *     aligned.  The caller owns every buffer; the library keeps no pointer after a call
  *     returns and allocates no device memory.
- *   - `dtype` is MI_ATTN_BF16 or MI_ATTN_F32 and applies to q, k, v and out alike.
- *     bf16 inputs are multiplied on matrix cores with fp32 accumulation; the softmax
- *     runs in fp32; bf16 outputs are rounded to nearest even.
+ *   - `dtype` is MI_ATTN_BF16, MI_ATTN_F16 or MI_ATTN_F32 and applies to q, k, v and out
+ *     alike (and to the new rows and caches of the decode calls).  bf16 and fp16 inputs
+ *     are multiplied on matrix cores with fp32 accumulation; the softmax runs in fp32;
+ *     16-bit outputs are rounded to nearest even.  fp16 follows the `_f16` twins of the
+ *     ripvec-core `Driver` page (`fused_scale_mask_softmax_f16` and the others: half
+ *     storage, fp32 reductions).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue work and
  *     never synchronise; errors raised while the kernels run surface at the caller's
  *     next synchronisation of that stream.
@@ -54,9 +57,9 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_VERSION 3
+#define MI_ATTN_VERSION 4
 
-typedef enum { MI_ATTN_F32 = 0, MI_ATTN_BF16 = 1 } mi_attn_dtype;
+typedef enum { MI_ATTN_F32 = 0, MI_ATTN_BF16 = 1, MI_ATTN_F16 = 2 } mi_attn_dtype;
 
 typedef enum {
     MI_ATTN_OK = 0,

@@ -46,7 +46,7 @@ def _nan(dtype):
 
 
 def _bits(a: np.ndarray) -> np.ndarray:
-    return a.view(np.uint16) if a.dtype == np.uint16 else a.view(np.uint32)
+    return a.view(np.uint16) if a.itemsize == 2 else a.view(np.uint32)
 
 
 def _host(t, dtype) -> np.ndarray:
@@ -75,6 +75,7 @@ PER_ITEM_CASES = [
     (2, 4, 1, 300, 128, [300, 299], 17, "f32"),
     (3, 6, 2, 256, 64, [200, 50, 256], 0, "f32"),
     (64, 8, 8, 96, 64, [(37 * i) % 97 for i in range(64)], 0, "f32"),  # 512 units: one workgroup each
+    (4, 32, 8, 1024, 128, [1000, 1, 0, 1024], 7, "f16"),
 ]
 
 
@@ -110,6 +111,8 @@ APPEND_CASES = [
     (2, 4, 1, 300, 128, [299, 298], 17, "f32"),
     (3, 6, 2, 256, 64, [199, 49, 255], 0, "f32"),
     (64, 8, 8, 96, 64, [(37 * i) % 97 - 1 for i in range(64)], 0, "f32"),
+    (4, 32, 8, 1024, 128, [999, 0, 1023, 1024], 0, "f16"),
+    (3, 12, 4, 513, 64, [512, 99, 2], 64, "f16"),
 ]
 
 

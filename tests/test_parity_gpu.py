@@ -71,6 +71,12 @@ PREFILL_CASES = [
     (1, 4, 2, 600, 600, 128, False, 0, None, 200, "bf16"),
     (2, 8, 4, 300, 300, 128, True, 0, None, 0, "bf16"),
     (2, 8, 4, 300, 300, 64, True, 0, [300, 257], 0, "bf16"),
+    # fp16 inputs (the fp16 MFMA and fp16 rounding of P and the output)
+    (1, 8, 2, 257, 257, 128, True, 0, None, 0, "f16"),
+    (1, 4, 2, 600, 600, 128, False, 0, [555], 200, "f16"),
+    (2, 4, 4, 333, 333, 64, False, 0, None, 128, "f16"),
+    (3, 6, 3, 200, 200, 32, False, 0, [200, 1, 0], 0, "f16"),
+    (2, 2, 2, 100, 150, 64, True, 50, [150, 120], 0, "f16"),
 ]
 
 
@@ -113,6 +119,8 @@ DECODE_CASES = [
     # 512 (item, kv head) units: one workgroup per key range, no split and no combine pass
     (64, 8, 8, 96, 90, 64, 0, [(37 * i) % 91 for i in range(64)], 0, "f32"),
     (128, 8, 4, 64, 64, 128, 40, None, 9, "bf16"),
+    (4, 32, 8, 1024, 1000, 128, 999, None, 0, "f16"),
+    (3, 12, 4, 512, 512, 32, 0, [512, 100, 3], 64, "f16"),
 ]
 
 
@@ -213,7 +221,8 @@ def _sample_rows(rng, B, H, L, n_random, edges):
     return np.array(sorted(rows), np.int32)
 
 
-@pytest.mark.parametrize("name", ["tiny_causal_f32", "bert_base_padded", "banded_w128_s8192", "causal_gqa_s4096"])
+@pytest.mark.parametrize("name", ["tiny_causal_f32", "bert_base_padded", "banded_w128_s8192", "causal_gqa_s4096",
+                                  "causal_gqa_s4096_f16"])
 def test_named_prefill_workload(mi, ref, name):
     import torch
     w = W.WORKLOADS[name]
@@ -235,14 +244,15 @@ def test_named_prefill_workload(mi, ref, name):
         check(g[rows[:, 0], rows[:, 1], rows[:, 2]], want, w.dtype, name)
 
 
-def test_named_decode_workload(mi, ref):
+@pytest.mark.parametrize("name", ["gqa_decode_kv8192", "gqa_decode_kv8192_f16"])
+def test_named_decode_workload(mi, ref, name):
     import torch
-    w = W.WORKLOADS["gqa_decode_kv8192"]
-    say("workload gqa_decode_kv8192")
+    w = W.WORKLOADS[name]
+    say(f"workload {name}")
     x = W.make_inputs(w)
     got = mi.attn_decode(to_gpu(x["q"]), to_gpu(x["k"]), to_gpu(x["v"]), kv_len=w.kv_len, pos_offset=w.pos_offset,
                          window=w.window, scale=w.attn_scale)
     torch.cuda.synchronize()
     want = ref.decode(x["q"], x["k"], x["v"], kv_len=w.kv_len, scale=w.attn_scale, pos_offset=w.pos_offset,
                       window=w.window)
-    check(to_f64(got), want, w.dtype, "gqa_decode_kv8192")
+    check(to_f64(got), want, w.dtype, name)

@@ -60,6 +60,8 @@ VARLEN_CASES = [
     ([150, 99], 4, 2, 64, True, 0, "f32"),
     ([65, 130], 2, 1, 128, False, 9, "f32"),
     ([100, 33, 0, 7], 4, 4, 32, True, 16, "f32"),
+    ([300, 0, 17, 513], 4, 4, 64, False, 0, "f16"),
+    ([257, 1, 300], 8, 2, 128, True, 0, "f16"),
 ]
 
 

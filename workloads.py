@@ -39,7 +39,7 @@ BF16_NAN = np.uint16(0x7FC0)
 
 
 def draw(rng: np.random.Generator, shape, sigma: float, dtype: str) -> np.ndarray:
-    """One tensor of i.i.d. N(0, sigma^2) values: float32, or bf16 bits (uint16)."""
+    """One tensor of i.i.d. N(0, sigma^2) values: float32, float16, or bf16 bits (uint16)."""
     x = rng.standard_normal(shape, dtype=np.float32)
     if sigma != 1.0:
         x *= np.float32(sigma)
@@ -47,6 +47,8 @@ def draw(rng: np.random.Generator, shape, sigma: float, dtype: str) -> np.ndarra
         return x
     if dtype == "bf16":
         return bf16_bits_from_f32(x)
+    if dtype == "f16":
+        return x.astype(np.float16)   # numpy rounds to nearest, ties to even
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -60,7 +62,7 @@ class Workload:
     q_len: int                # 1 for decode
     kv_len: int
     head_dim: int
-    dtype: str                # "f32" or "bf16"
+    dtype: str                # "f32", "bf16" or "f16"
     sigma: float
     causal: bool
     window: int = 0
@@ -86,6 +88,11 @@ WORKLOADS = {
                                  True, scale=1.0 / math.sqrt(128), seed=4),
     "gqa_decode_kv8192": Workload("gqa_decode_kv8192", "decode", 64, 32, 8, 1, 8192, 128, "bf16", 1.0,
                                   True, pos_offset=8191, capacity=8192, seed=5),
+    # the causal GQA prefill and the GQA decode with fp16 inputs (the pages' _f16 twins)
+    "causal_gqa_s4096_f16": Workload("causal_gqa_s4096_f16", "prefill", 1, 32, 8, 4096, 4096, 128, "f16", 0.5,
+                                     True, scale=1.0 / math.sqrt(128), seed=4),
+    "gqa_decode_kv8192_f16": Workload("gqa_decode_kv8192_f16", "decode", 64, 32, 8, 1, 8192, 128, "f16", 1.0,
+                                      True, pos_offset=8191, capacity=8192, seed=5),
     # the BERT-shaped batch without padding: the same item lengths, tokens concatenated
     # token-major ([tokens, heads, head_dim]) with cu_seqlens boundaries
     "bert_base_varlen": Workload("bert_base_varlen", "prefill_varlen", 32, 12, 12, 512, 512, 64, "bf16", 1.0,
