@@ -114,6 +114,18 @@ class Oracle:
         self.threads_used = ret
         return out
 
+    def prefill_token_major(self, q, k, v, *, scale: float, causal: bool = False, pos_offset: int = 0,
+                            seq_lens=None, window: int = 0, nthreads: int | None = None) -> np.ndarray:
+        """The prefill definition on token-major tensors: q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D]
+        -> [B,Lq,Hq,D] float64 (the layout before ferrum-kernels Backend's head-major
+        conversion and after its `transpose_head_to_token`)."""
+        qh = np.ascontiguousarray(np.asarray(q).transpose(0, 2, 1, 3))
+        kh = np.ascontiguousarray(np.asarray(k).transpose(0, 2, 1, 3))
+        vh = np.ascontiguousarray(np.asarray(v).transpose(0, 2, 1, 3))
+        out = self.prefill(qh, kh, vh, scale=scale, causal=causal, pos_offset=pos_offset, seq_lens=seq_lens,
+                           window=window, nthreads=nthreads)
+        return np.ascontiguousarray(out.transpose(0, 2, 1, 3))
+
     def prefill_varlen(self, q, k, v, cu_seqlens, *, scale: float, causal: bool = False, window: int = 0,
                        nthreads: int | None = None) -> np.ndarray:
         """Unpadded batch (ripvec-core `Driver`, `prepare_batch_unpadded`): tokens of all

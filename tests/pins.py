@@ -598,4 +598,30 @@ def pin_f16_widening(oracle):
     _close(a, b, 0.0, "fp16 vs widened fp32")
 
 
+def pin_token_major_brute_force(oracle):
+    """Token-major prefill == brute force on head-major copies built element by element."""
+    rng = _rng(560)
+    B, Lq, Lk, Hq, Hkv, D = 2, 5, 7, 4, 2, 4
+    q = draw(rng, (B, Lq, Hq, D), 1.0, "f32")
+    k = draw(rng, (B, Lk, Hkv, D), 1.0, "f32")
+    v = draw(rng, (B, Lk, Hkv, D), 1.0, "f32")
+    got = oracle.prefill_token_major(q, k, v, scale=0.6, causal=True, pos_offset=2, seq_lens=[7, 5], window=4)
+    qh = np.zeros((B, Hq, Lq, D), np.float32)
+    kh = np.zeros((B, Hkv, Lk, D), np.float32)
+    vh = np.zeros((B, Hkv, Lk, D), np.float32)
+    for b in range(B):
+        for t in range(Lq):
+            for h in range(Hq):
+                qh[b, h, t] = q[b, t, h]
+        for t in range(Lk):
+            for h in range(Hkv):
+                kh[b, h, t] = k[b, t, h]
+                vh[b, h, t] = v[b, t, h]
+    ref = np.array(brute.attention(qh, kh, vh, scale=0.6, causal=True, pos_offset=2, seq_lens=[7, 5], window=4))
+    for b in range(B):
+        for t in range(Lq):
+            for h in range(Hq):
+                _close(got[b, t, h], ref[b, h, t], 1e-12, f"token-major item {b} token {t} head {h}")
+
+
 PINS = {name[4:]: fn for name, fn in sorted(globals().items()) if name.startswith("pin_") and callable(fn)}

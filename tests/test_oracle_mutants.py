@@ -134,7 +134,18 @@ class _VarlenHeadsAsTokens(oracle.Oracle):
         return out
 
 
-PY_MUTANTS = {c.__name__[1:]: c for c in (_AppendOneLate, _AppendKVSwapped, _AppendModifiesInput,
+class _TokenMajorNoTranspose(oracle.Oracle):
+    def prefill_token_major(self, q, k, v, *, scale, causal=False, pos_offset=0, seq_lens=None, window=0,
+                            nthreads=None):
+        B, Lq, Hq, D = q.shape
+        _, Lk, Hkv, _ = k.shape
+        out = self.prefill(np.ascontiguousarray(q).reshape(B, Hq, Lq, D), np.ascontiguousarray(k).reshape(B, Hkv, Lk, D),
+                           np.ascontiguousarray(v).reshape(B, Hkv, Lk, D), scale=scale, causal=causal,
+                           pos_offset=pos_offset, seq_lens=seq_lens, window=window)
+        return out.reshape(B, Lq, Hq, D)
+
+
+PY_MUTANTS = {c.__name__[1:]: c for c in (_TokenMajorNoTranspose, _AppendOneLate, _AppendKVSwapped, _AppendModifiesInput,
                                           _NewKeyNotAttended, _NoRoomAttendsAll, _PerCacheItemsRotated,
                                           _VarlenItemOneLonger, _VarlenHeadsAsTokens)}
 
