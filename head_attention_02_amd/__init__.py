@@ -8,6 +8,8 @@ missing library or GPU raises.
 
     attn_prefill(q, k, v, out=None, *, pos_offset=0, seq_lens=None, window=0,
                  causal=False, scale=None)
+    attn_prefill_token_major(q, k, v, out=None, *, pos_offset=0, seq_lens=None, window=0,
+                             causal=False, scale=None)
     attn_prefill_varlen(q, k, v, cu_seqlens, max_seqlen=None, out=None, *, window=0,
                         causal=False, scale=None)
     attn_decode(q, k_cache, v_cache, out=None, *, kv_len=None, pos_offset=None,
@@ -20,7 +22,8 @@ missing library or GPU raises.
     attn_last_error(), attn_version()
 
 Layouts: q [batch, q_heads, q_len, head_dim]; k, v [batch, kv_heads, kv_len, head_dim]
-(unpadded: q, out [tokens, q_heads, head_dim], k, v [tokens, kv_heads, head_dim]);
+(token-major: q, out [batch, q_len, q_heads, head_dim], k, v [batch, kv_len, kv_heads,
+head_dim]; unpadded: q, out [tokens, q_heads, head_dim], k, v [tokens, kv_heads, head_dim]);
 decode caches [batch, kv_heads, capacity, head_dim] (head-major); the per-cache calls
 take one [kv_heads, capacity, head_dim] cache per item.  scale defaults to
 1/sqrt(head_dim).
@@ -36,7 +39,7 @@ LIBRARY = Path(__file__).resolve().parent / "libmi_attn.so"
 MI_ATTN_F32, MI_ATTN_BF16, MI_ATTN_F16 = 0, 1, 2
 MI_ATTN_OK, MI_ATTN_ERR_INVALID, MI_ATTN_ERR_UNSUPPORTED, MI_ATTN_ERR_HIP = 0, 1, 2, 3
 
-EXPORTS = ("attn_prefill", "attn_prefill_varlen", "attn_decode", "attn_decode_per_cache", "attn_decode_append",
+EXPORTS = ("attn_prefill", "attn_prefill_token_major", "attn_prefill_varlen", "attn_decode", "attn_decode_per_cache", "attn_decode_append",
            "attn_decode_workspace_bytes", "attn_last_error", "attn_version")
 
 
@@ -59,6 +62,8 @@ def library() -> ctypes.CDLL:
         vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         lib.attn_prefill.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, i, i, f, i, vp]
         lib.attn_prefill.restype = i
+        lib.attn_prefill_token_major.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, i, i, f, i, vp]
+        lib.attn_prefill_token_major.restype = i
         lib.attn_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
         lib.attn_prefill_varlen.restype = i
         lib.attn_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, i, f, i, vp, sz, vp]
@@ -133,11 +138,26 @@ def _stream(stream):
 def attn_prefill(q, k, v, out=None, *, pos_offset: int = 0, seq_lens=None, window: int = 0,
                  causal: bool = False, scale: float | None = None, stream=None):
     """Prefill attention; returns `out` [batch, q_heads, q_len, head_dim]."""
+    return _prefill_padded(False, q, k, v, out, pos_offset, seq_lens, window, causal, scale, stream)
+
+
+def attn_prefill_token_major(q, k, v, out=None, *, pos_offset: int = 0, seq_lens=None, window: int = 0,
+                             causal: bool = False, scale: float | None = None, stream=None):
+    """Prefill attention on token-major tensors: q [batch, q_len, q_heads, head_dim], k, v
+    [batch, kv_len, kv_heads, head_dim]; returns `out` [batch, q_len, q_heads, head_dim]."""
+    return _prefill_padded(True, q, k, v, out, pos_offset, seq_lens, window, causal, scale, stream)
+
+
+def _prefill_padded(token_major, q, k, v, out, pos_offset, seq_lens, window, causal, scale, stream):
     torch = _torch()
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
-        raise ValueError("q must be [B,Hq,Lq,D] and k, v [B,Hkv,Lk,D]")
-    B, Hq, Lq, D = q.shape
-    Bk, Hkv, Lk, Dk = k.shape
+        raise ValueError("q and k, v must be 4-D of one layout, k and v of one shape")
+    if token_major:
+        B, Lq, Hq, D = q.shape
+        Bk, Lk, Hkv, Dk = k.shape
+    else:
+        B, Hq, Lq, D = q.shape
+        Bk, Hkv, Lk, Dk = k.shape
     if Bk != B or Dk != D:
         raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree on batch or head_dim")
     dt = _dtype_code(q)
@@ -151,9 +171,9 @@ def attn_prefill(q, k, v, out=None, *, pos_offset: int = 0, seq_lens=None, windo
         raise ValueError("seq_lens must be an int32 tensor of batch elements")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    st = library().attn_prefill(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), B, Hq, Hkv, Lq, Lk,
-                                D, pos_offset, _dev(seq_lens, "seq_lens"), window, int(bool(causal)),
-                                float(scale), dt, _stream(stream))
+    fn = library().attn_prefill_token_major if token_major else library().attn_prefill
+    st = fn(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), B, Hq, Hkv, Lq, Lk, D, pos_offset,
+            _dev(seq_lens, "seq_lens"), window, int(bool(causal)), float(scale), dt, _stream(stream))
     _check(st)
     return out
 

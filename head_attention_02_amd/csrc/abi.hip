@@ -27,18 +27,12 @@ bool supported_head_dim(int d) { return d == 32 || d == 64 || d == 128; }
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-int attn_version(void) { return MI_ATTN_VERSION; }
-
-const char* attn_last_error(void) { return g_error; }
-
-int attn_prefill(const void* q, const void* k, const void* v, void* out, int batch, int q_heads,
-                 int kv_heads, int q_len, int kv_len, int head_dim, int pos_offset,
-                 const int32_t* seq_lens, int window, int causal, float scale, int dtype,
-                 void* stream) {
+int prefill_padded(const char* fn, int token_major, const void* q, const void* k, const void* v, void* out,
+                   int batch, int q_heads, int kv_heads, int q_len, int kv_len, int head_dim, int pos_offset,
+                   const int32_t* seq_lens, int window, int causal, float scale, int dtype, void* stream) {
     g_error[0] = '\0';
-    const char* fn = "attn_prefill";
     if (dtype != MI_ATTN_BF16 && dtype != MI_ATTN_F32 && dtype != MI_ATTN_F16)
         return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
     if (batch < 0 || q_len < 0 || kv_len < 0)
@@ -81,12 +75,38 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int bat
     a.window = window;
     a.causal = causal ? 1 : 0;
     a.scale = scale;
+    a.token_major = token_major;
     hipStream_t s = (hipStream_t)stream;
     a.f16 = dtype == MI_ATTN_F16;
     hipError_t e = dtype != MI_ATTN_F32 ? mi_attn::launch_prefill_bf16(a, head_dim, s)
                                         : mi_attn::launch_prefill_f32(a, head_dim, s);
     if (e != hipSuccess) return fail(MI_ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return MI_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_version(void) { return MI_ATTN_VERSION; }
+
+const char* attn_last_error(void) { return g_error; }
+
+
+int attn_prefill(const void* q, const void* k, const void* v, void* out, int batch, int q_heads,
+                 int kv_heads, int q_len, int kv_len, int head_dim, int pos_offset,
+                 const int32_t* seq_lens, int window, int causal, float scale, int dtype,
+                 void* stream) {
+    return prefill_padded("attn_prefill", 0, q, k, v, out, batch, q_heads, kv_heads, q_len, kv_len, head_dim,
+                          pos_offset, seq_lens, window, causal, scale, dtype, stream);
+}
+
+int attn_prefill_token_major(const void* q, const void* k, const void* v, void* out, int batch, int q_heads,
+                             int kv_heads, int q_len, int kv_len, int head_dim, int pos_offset,
+                             const int32_t* seq_lens, int window, int causal, float scale, int dtype,
+                             void* stream) {
+    return prefill_padded("attn_prefill_token_major", 1, q, k, v, out, batch, q_heads, kv_heads, q_len, kv_len,
+                          head_dim, pos_offset, seq_lens, window, causal, scale, dtype, stream);
 }
 
 int attn_prefill_varlen(const void* q, const void* k, const void* v, void* out, const int32_t* cu_seqlens,

@@ -24,6 +24,9 @@ struct PrefillArgs {
     float scale;
     int n_qtiles;             // grid.x
     int f16;                  // 16-bit inputs: 0 = bf16, 1 = fp16 (matrix-core kernels)
+    // Padded layout only: 1 = token-major, q and out [batch, q_len, q_heads, D] and k, v
+    // [batch, kv_len, kv_heads, D]; 0 = head-major [batch, heads, len, D].
+    int token_major;
 };
 
 // Where one (item, query head)'s rows live and how many there are (element offsets and
@@ -47,6 +50,13 @@ __device__ __forceinline__ ItemRows item_rows(const PrefillArgs& a, int b, int h
         r.kv_base = (size_t)t0 * r.kv_rs + (size_t)kvh * D;
         r.q_len = n;
         r.kv_valid = n;
+    } else if (a.token_major) {
+        r.q_rs = a.q_heads * D;
+        r.kv_rs = a.kv_heads * D;
+        r.q_base = (size_t)b * a.q_len * r.q_rs + (size_t)h * D;
+        r.kv_base = (size_t)b * a.kv_len * r.kv_rs + (size_t)kvh * D;
+        r.q_len = a.q_len;
+        r.kv_valid = a.seq_lens ? min(max(a.seq_lens[b], 0), a.kv_len) : a.kv_len;
     } else {
         r.q_rs = D;
         r.kv_rs = D;

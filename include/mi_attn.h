@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_VERSION 4
+#define MI_ATTN_VERSION 5
 
 typedef enum { MI_ATTN_F32 = 0, MI_ATTN_BF16 = 1, MI_ATTN_F16 = 2 } mi_attn_dtype;
 
@@ -94,6 +94,26 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int bat
                  int kv_heads, int q_len, int kv_len, int head_dim, int pos_offset,
                  const int32_t* seq_lens, int window, int causal, float scale, int dtype,
                  void* stream);
+
+/*
+ * attn_prefill_token_major -- attn_prefill with every tensor token-major: the layout
+ * the heads come in from the QKV projection and go out in to the output projection.
+ * Follows the ferrum-kernels `Backend` page, where `flash_attention` runs between a
+ * token-major -> head-major conversion of its inputs (`qk_norm_rope`: input
+ * [tokens, heads, head_dim], output head-major) and `transpose_head_to_token`
+ * ([heads, tokens, dim] -> [tokens, heads, dim], called after flash_attention to restore
+ * token-major layout for O-proj), and the ripvec-core `Driver` page's `attn_reshape`
+ * ([batch, num_heads, seq, head_dim] -> [batch * seq, hidden]); here neither
+ * transpose exists.
+ *
+ *   q, out  [batch, q_len,  q_heads,  head_dim]
+ *   k, v    [batch, kv_len, kv_heads, head_dim]
+ *   Every other argument, and every rule, is attn_prefill's.
+ */
+int attn_prefill_token_major(const void* q, const void* k, const void* v, void* out, int batch, int q_heads,
+                             int kv_heads, int q_len, int kv_len, int head_dim, int pos_offset,
+                             const int32_t* seq_lens, int window, int causal, float scale, int dtype,
+                             void* stream);
 
 /*
  * attn_prefill_varlen -- attn_prefill on an unpadded batch: the items' tokens are

@@ -199,3 +199,20 @@ def test_prefill_varlen_validation(kw, status, msg):
 def test_prefill_varlen_empty_calls_are_ok_without_a_gpu():
     assert varlen(batch=0, cu=None) == mi.MI_ATTN_OK
     assert varlen(max_seqlen=0, q=None) == mi.MI_ATTN_OK
+
+
+def test_token_major_prefill_validation():
+    lib = mi.library()
+    args = [FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 16, 16, 64, 0, None, 0, 1, 0.125, mi.MI_ATTN_BF16, None]
+    bad = list(args)
+    bad[5] = 6   # q_heads not a multiple of kv_heads... 6 % 2 == 0, so use kv_heads 4
+    bad[6] = 4
+    assert lib.attn_prefill_token_major(*bad) == mi.MI_ATTN_ERR_INVALID
+    assert mi.attn_last_error().startswith("attn_prefill_token_major: ") and "not a multiple" in mi.attn_last_error()
+    bad = list(args)
+    bad[10] = 9   # pos_offset + q_len > kv_len
+    assert lib.attn_prefill_token_major(*bad) == mi.MI_ATTN_ERR_INVALID
+    assert "exceeds kv_len" in mi.attn_last_error()
+    empty = list(args)
+    empty[4] = 0
+    assert lib.attn_prefill_token_major(*empty) == mi.MI_ATTN_OK
