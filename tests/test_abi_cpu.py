@@ -216,3 +216,25 @@ def test_token_major_prefill_validation():
     empty = list(args)
     empty[4] = 0
     assert lib.attn_prefill_token_major(*empty) == mi.MI_ATTN_OK
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """The binding has no fallback: with the library absent, loading it raises."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("mi_copy", mi.__file__)
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    m.LIBRARY = tmp_path / "libmi_attn.so"
+    m._lib = None
+    with pytest.raises(RuntimeError, match="not built"):
+        m.library()
+    with pytest.raises(RuntimeError, match="not built"):
+        m.attn_version()
+
+
+def test_binding_sources_hold_no_attention_arithmetic():
+    """The binding marshals arguments only: no softmax, exp or matmul of its own, and it
+    never imports the oracle."""
+    src = Path(mi.__file__).read_text()
+    for word in ("softmax", "exp(", "matmul", "@", "einsum", "import oracle", "scaled_dot_product"):
+        assert word not in src, word
