@@ -284,11 +284,11 @@ def copy_calibration(steps: int, warmup: int) -> int:
 
 # (run label, workload, kernel-name prefixes that make up one call, kernel sources)
 TRAFFIC_RUNS = [
-    ("head", "causal_gqa_s4096", ["prefill_bf16_kernel<128"], ["prefill_bf16.hip", "mi_attn_device.hpp"]),
+    ("head", "causal_gqa_s4096", ["prefill_bf16_kernel<128"], ["prefill_bf16.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]),
     ("head", "gqa_decode_kv8192", ["decode_split_kernel<128", "decode_combine_kernel<128"],
-     ["decode.hip", "mi_attn_device.hpp"]),
+     ["decode.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]),
     ("append", "gqa_decode_append_kv8192", ["decode_split_kernel<128", "decode_combine_kernel<128"],
-     ["decode.hip", "mi_attn_device.hpp"]),
+     ["decode.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]),
 ]
 
 
@@ -416,11 +416,11 @@ def main() -> int:
             fl = prefill_flops(w, x["seq_lens"])
             peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS   # fp16 dense = bf16 dense
             if w.dtype == "f32":
-                src = ["prefill_f32.hip", "mi_attn_device.hpp"]
+                src = ["prefill_f32.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]
             elif w.head_dim == 128:
-                src = ["prefill_bf16.hip", "mi_attn_device.hpp"]
+                src = ["prefill_bf16.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]
             else:
-                src = ["prefill_bf16_narrow.hip", "mi_attn_device.hpp"]
+                src = ["prefill_bf16_narrow.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]
             rooflines[w.name] = {"bound": "mfma", "achieved": fl / sec / 1e12, "peak": peak, "unit": "TFLOP/s",
                                  "frac": fl / sec / 1e12 / peak,
                                  "traffic": traffic_from_profiles(w.name, kernel_sources_digest(src)),
@@ -429,7 +429,7 @@ def main() -> int:
                                  "hbm_GBps": prefill_bytes(w, x["seq_lens"]) / sec / 1e9}
         else:
             by = decode_bytes(w)
-            src = ["decode.hip", "mi_attn_device.hpp"]
+            src = ["decode.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]
             rooflines[w.name] = {"bound": "hbm", "achieved": by / sec / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                  "frac": by / sec / 1e9 / PEAK_HBM_GBPS,
                                  "traffic": traffic_from_profiles(w.name, kernel_sources_digest(src)),
