@@ -403,14 +403,16 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = begin.elapsed_time(end) / K
-    kernel_ms = [float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)])) for i in range(len(runners))]
+    per_launch = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)] for i in range(len(runners))]
+    kernel_ms = [float(np.mean(t)) for t in per_launch]
+    spread = [{"kernel_ms_median": float(np.median(t)), "kernel_ms_min": float(np.min(t))} for t in per_launch]
 
     result = {"metric": "attention TFLOP/s (prefill, % MFMA peak); decode KV GB/s (% HBM peak)",
               "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": step_ms,
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
               "data": "synthetic (seeded N(0, sigma^2), bf16 by round-to-nearest-even)"}
     rooflines = {}
-    for w, x, ms in zip(ws, inputs, kernel_ms):
+    for w, x, ms, sp in zip(ws, inputs, kernel_ms, spread):
         sec = ms / 1e3
         if w.kind in ("prefill", "prefill_varlen"):
             fl = prefill_flops(w, x["seq_lens"])
@@ -424,7 +426,7 @@ def main() -> int:
             rooflines[w.name] = {"bound": "mfma", "achieved": fl / sec / 1e12, "peak": peak, "unit": "TFLOP/s",
                                  "frac": fl / sec / 1e12 / peak,
                                  "traffic": traffic_from_profiles(w.name, kernel_sources_digest(src)),
-                                 "kernel_ms": ms, "algorithmic_flop": fl,
+                                 "kernel_ms": ms, **sp, "algorithmic_flop": fl,
                                  "algorithmic_bytes": prefill_bytes(w, x["seq_lens"]),
                                  "hbm_GBps": prefill_bytes(w, x["seq_lens"]) / sec / 1e9}
         else:
@@ -433,7 +435,7 @@ def main() -> int:
             rooflines[w.name] = {"bound": "hbm", "achieved": by / sec / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                  "frac": by / sec / 1e9 / PEAK_HBM_GBPS,
                                  "traffic": traffic_from_profiles(w.name, kernel_sources_digest(src)),
-                                 "kernel_ms": ms, "algorithmic_bytes": by,
+                                 "kernel_ms": ms, **sp, "algorithmic_bytes": by,
                                  "algorithmic_flop": decode_flops(w)}
     head = ws[0]
     r0 = rooflines[head.name]
