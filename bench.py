@@ -114,7 +114,7 @@ class Runner:
         self.mi, self.w = mi, w
         self.q, self.k, self.v = to_gpu(x["q"]), to_gpu(x["k"]), to_gpu(x["v"])
         self.out = torch.empty_like(self.q)
-        lens = x.get("seq_lens") if w.kind == "prefill" else x.get("kv_lens")
+        lens = x.get("seq_lens") if w.kind in ("prefill", "prefill_token_major") else x.get("kv_lens")
         if w.kind == "prefill_varlen":
             self.cu = to_gpu(x["cu_seqlens"])
             self.max_seqlen = int(np.max(x["seq_lens"]))
@@ -133,6 +133,9 @@ class Runner:
         if w.kind == "prefill":
             self.mi.attn_prefill(self.q, self.k, self.v, self.out, pos_offset=w.pos_offset, seq_lens=self.lens,
                                  window=w.window, causal=w.causal, scale=w.attn_scale)
+        elif w.kind == "prefill_token_major":
+            self.mi.attn_prefill_token_major(self.q, self.k, self.v, self.out, pos_offset=w.pos_offset,
+                                             seq_lens=self.lens, window=w.window, causal=w.causal, scale=w.attn_scale)
         elif w.kind == "prefill_varlen":
             self.mi.attn_prefill_varlen(self.q, self.k, self.v, self.cu, self.max_seqlen, self.out, window=w.window,
                                         causal=w.causal, scale=w.attn_scale)
@@ -197,6 +200,8 @@ def cpu_baseline_prefill(w: W.Workload, x: dict, budget_s: float) -> dict:
     import oracle
     if w.kind == "prefill_varlen":
         return cpu_baseline_varlen(w, x, budget_s)
+    if w.kind == "prefill_token_major":   # the oracle's rows entry reads head-major arrays
+        x = dict(x, **{n: np.ascontiguousarray(x[n].transpose(0, 2, 1, 3)) for n in ("q", "k", "v")})
     ref = oracle.default()
     nt = len(os.sched_getaffinity(0))
     rng = np.random.default_rng(123)
@@ -414,7 +419,7 @@ def main() -> int:
     rooflines = {}
     for w, x, ms, sp in zip(ws, inputs, kernel_ms, spread):
         sec = ms / 1e3
-        if w.kind in ("prefill", "prefill_varlen"):
+        if w.kind in ("prefill", "prefill_token_major", "prefill_varlen"):
             fl = prefill_flops(w, x["seq_lens"])
             peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS   # fp16 dense = bf16 dense
             if w.dtype == "f32":
@@ -458,7 +463,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (cpu_baseline)")
         for w, x in zip(ws, inputs):
-            if w.kind in ("prefill", "prefill_varlen"):
+            if w.kind in ("prefill", "prefill_token_major", "prefill_varlen"):
                 result.setdefault("cpu_baseline", cpu_baseline_prefill(w, x, args.cpu_budget))
             else:
                 key = "cpu_baseline" if "cpu_baseline" not in result else "cpu_baseline_decode"

@@ -75,6 +75,25 @@ def test_token_major_parity(mi, ref, case):
     assert torch.equal(got, hm.transpose(1, 2).contiguous()), "token-major and head-major launches differ"
 
 
+def test_named_token_major_workload(mi, ref):
+    """The causal GQA prefill (1 x 4096 tokens, 32/8 heads, head_dim 128) on token-major
+    tensors, in the benchmark's launch configuration: sampled rows against the oracle."""
+    import torch
+    w = W.WORKLOADS["causal_gqa_s4096_token_major"]
+    say("workload causal_gqa_s4096_token_major")
+    x = W.make_inputs(w)
+    got = mi.attn_prefill_token_major(to_gpu(x["q"]), to_gpu(x["k"]), to_gpu(x["v"]), causal=w.causal,
+                                      scale=w.attn_scale)
+    torch.cuda.synchronize()
+    g = to_f64(got)
+    hm = {n: np.ascontiguousarray(x[n].transpose(0, 2, 1, 3)) for n in ("q", "k", "v")}
+    rng = np.random.default_rng(5)
+    rows = np.stack([np.zeros(300, np.int64), rng.integers(0, w.q_heads, 300), rng.integers(0, w.q_len, 300)], 1)
+    rows = np.concatenate([rows, [[0, 0, 0], [0, 31, 4095]]]).astype(np.int32)
+    want = ref.prefill(hm["q"], hm["k"], hm["v"], scale=w.attn_scale, causal=True, rows=rows)
+    check(g[rows[:, 0], rows[:, 2], rows[:, 1]], want, w.dtype, w.name)
+
+
 def test_long_decode_cache(mi, ref):
     """One item, one kv head, 262144 cached positions (head_dim 128, bf16): the split plan
     cuts the range into many splits; checked against the oracle."""

@@ -55,7 +55,7 @@ def draw(rng: np.random.Generator, shape, sigma: float, dtype: str) -> np.ndarra
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "prefill", "prefill_varlen", "decode" or "decode_append"
+    kind: str                 # "prefill", "prefill_token_major", "prefill_varlen", "decode" or "decode_append"
     batch: int
     q_heads: int
     kv_heads: int
@@ -93,6 +93,9 @@ WORKLOADS = {
                                      True, scale=1.0 / math.sqrt(128), seed=4),
     "gqa_decode_kv8192_f16": Workload("gqa_decode_kv8192_f16", "decode", 64, 32, 8, 1, 8192, 128, "f16", 1.0,
                                       True, pos_offset=8191, capacity=8192, seed=5),
+    # the causal GQA prefill on token-major tensors q/out [B, L, Hq, D], k/v [B, L, Hkv, D]
+    "causal_gqa_s4096_token_major": Workload("causal_gqa_s4096_token_major", "prefill_token_major", 1, 32, 8, 4096,
+                                             4096, 128, "bf16", 0.5, True, scale=1.0 / math.sqrt(128), seed=4),
     # the BERT-shaped batch without padding: the same item lengths, tokens concatenated
     # token-major ([tokens, heads, head_dim]) with cu_seqlens boundaries
     "bert_base_varlen": Workload("bert_base_varlen", "prefill_varlen", 32, 12, 12, 512, 512, 64, "bf16", 1.0,
@@ -108,6 +111,7 @@ def make_inputs(w: Workload) -> dict:
     """Arrays for a workload, in the draw order of the recipe above.
 
     prefill: q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D], seq_lens [B] int32 or None
+    prefill_token_major: q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D], seq_lens as for prefill
     prefill_varlen: q [T,Hq,D], k/v [T,Hkv,D] token-major over the items' T tokens (drawn
              after the lengths), seq_lens [B], cu_seqlens [B+1] int32
     decode:  q [B,Hq,D], k/v caches [B,Hkv,capacity,D], kv_lens None
@@ -128,6 +132,11 @@ def make_inputs(w: Workload) -> dict:
         k = draw(rng, (T, w.kv_heads, w.head_dim), w.sigma, w.dtype)
         v = draw(rng, (T, w.kv_heads, w.head_dim), w.sigma, w.dtype)
         return {"q": q, "k": k, "v": v, "seq_lens": lens, "cu_seqlens": cu}
+    if w.kind == "prefill_token_major":
+        q = draw(rng, (w.batch, w.q_len, w.q_heads, w.head_dim), w.sigma, w.dtype)
+        k = draw(rng, (w.batch, w.kv_len, w.kv_heads, w.head_dim), w.sigma, w.dtype)
+        v = draw(rng, (w.batch, w.kv_len, w.kv_heads, w.head_dim), w.sigma, w.dtype)
+        return {"q": q, "k": k, "v": v, "seq_lens": seq_lens}
     if w.kind == "prefill":
         q = draw(rng, (w.batch, w.q_heads, w.q_len, w.head_dim), w.sigma, w.dtype)
         k = draw(rng, (w.batch, w.kv_heads, w.kv_len, w.head_dim), w.sigma, w.dtype)
