@@ -49,6 +49,8 @@
 // rows at one 64-byte column group, so V rows are XOR-swizzled at 64-byte granularity:
 // chunk c of row r sits at chunk c ^ vswz(r), which puts the four rows in four
 // different quarters of the 256 bytes the banks cover.
+#include <type_traits>
+
 #include "mi_attn_device.hpp"
 #include "mi_attn_kernels.hpp"
 
@@ -268,6 +270,10 @@ struct Prefill {
     // then probabilities -> packed bf16 P^T operands and the row sum.  Element e of block
     // kb2 is key kt*64 + 32*kb2 + 8*(e/4) + 4*g + e%4; P chunk c4 (16 keys) = block c4/2,
     // elements 8*(c4%2) + [0, 8).
+    // FULL: the caller knows that every row of the workgroup sees every key of tile kt
+    // (then no wave can skip it and no element needs a test), and the phase runs without
+    // those checks and their branches.
+    template <bool FULL = false>
     __device__ __forceinline__ void vector_phase(int kt) {
         // Issue priority: the other wave on this SIMD is in its matrix phase.  The vector
         // phase is a dense stream of independent VALU instructions, and MFMAs issue through
@@ -276,12 +282,12 @@ struct Prefill {
         // back priority 2 at its end -- before the barrier, so that the priority is already
         // in place when the following matrix phase starts.
         __builtin_amdgcn_s_setprio(0);
-        if (!wave_sees(kt)) {   // no score of this tile was computed, and none is used
+        if (!FULL && !wave_sees(kt)) {   // no score of this tile was computed, and none is used
             __builtin_amdgcn_s_setprio(2);
             return;
         }
         const int kbase = kt * kBN;
-        const bool full = all_rows_valid && kbase >= inter_lo && kbase + kBN - 1 <= inter_hi;
+        const bool full = FULL || (all_rows_valid && kbase >= inter_lo && kbase + kBN - 1 <= inter_hi);
         if (!full) {
             keep_branch();
             const int lo = lo_r - kbase - 4 * g, hi = hi_r - kbase - 4 * g;
@@ -408,6 +414,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     if (p_lo >= valid) k_end = k_begin;       // every row of the tile is padding
     const int kt_begin = k_begin / kBN;
     const int kt_end = k_end > k_begin ? (k_end + kBN - 1) / kBN : kt_begin;
+    // Key tiles every row of the workgroup sees in full: [full_lo, full_hi] (keys).
+    int full_lo = 0, full_hi = valid - 1;
+    if (a.causal) full_hi = min(full_hi, p_lo);
+    if (a.window > 0) {
+        if (a.causal) {
+            full_lo = max(0, p_hi - a.window + 1);
+        } else {
+            full_lo = max(0, p_hi - half_w);
+            full_hi = min(full_hi, p_lo + half_w);
+        }
+    }
+    if (p_hi >= valid || q0 + kBM > q_len) full_hi = -1;   // some row is padding or past the end
+    // the loop runs V(t) on tile kt_begin + t + 1, t in [0, n-1): tiles of t in [ta, tb) are full
+    const int nv = max(kt_end - kt_begin - 1, 0);   // vector phases in the loop
+    int ta = 0, tb = 0;
+    if (full_hi >= full_lo) {
+        const int f0 = (full_lo + kBN - 1) / kBN, f1 = (full_hi + 1) / kBN;   // full tiles [f0, f1)
+        ta = min(max(f0 - kt_begin - 1, 0), nv);
+        tb = min(max(f1 - kt_begin - 1, ta), nv);
+    }
+    typedef std::integral_constant<bool, true> T_;
+    typedef std::integral_constant<bool, false> F_;
 
     // ---- this lane's query row and key interval, the wave's common keys ----------------
     const int r0 = q0 + wave * 32;
@@ -524,12 +552,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
             slot_end(false);
             st.vector_phase(kt_begin);                                 // slot 1: V(-1)
             slot_end(true);
-            for (int t = 0; t + 1 < n; ++t) {
+            auto body0 = [&](int t, auto full_c) {
                 st.matrix_phase(st.wave_sees(kt_begin + t + 1), kbuf(t + 1), st.wave_sees(kt_begin + t), vbuf(t));     // slot 2t+2: M(t)
                 slot_end(false);
-                st.vector_phase(kt_begin + t + 1);                     // slot 2t+3: V(t)
+                st.template vector_phase<decltype(full_c)::value>(kt_begin + t + 1);   // slot 2t+3: V(t)
                 slot_end(true);
-            }
+            };
+            int t = 0;
+            for (; t < ta; ++t) body0(t, F_{});
+            for (; t < tb; ++t) body0(t, T_{});
+            for (; t + 1 < n; ++t) body0(t, F_{});
             st.matrix_phase(false, kbuf(0), st.wave_sees(kt_begin + n - 1), vbuf(n - 1));        // slot 2n: M(n-1)
             slot_end(false);
             slot_end(true);                                            // slot 2n+1
@@ -541,13 +573,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
             copies(1);                                                 // slot 2: V(-1)
             st.vector_phase(kt_begin);
             slot_end(false);
-            for (int t = 0; t + 1 < n; ++t) {
+            auto body1 = [&](int t, auto full_c) {
                 st.matrix_phase(st.wave_sees(kt_begin + t + 1), kbuf(t + 1), st.wave_sees(kt_begin + t), vbuf(t));     // slot 2t+3: M(t)
                 slot_end(true);
                 copies(t + 2);                                         // slot 2t+4: V(t)
-                st.vector_phase(kt_begin + t + 1);
+                st.template vector_phase<decltype(full_c)::value>(kt_begin + t + 1);
                 slot_end(false);
-            }
+            };
+            int t = 0;
+            for (; t < ta; ++t) body1(t, F_{});
+            for (; t < tb; ++t) body1(t, T_{});
+            for (; t + 1 < n; ++t) body1(t, F_{});
             st.matrix_phase(false, kbuf(0), st.wave_sees(kt_begin + n - 1), vbuf(n - 1));        // slot 2n+1: M(n-1)
             slot_end(true);
             slot_end(false);                                           // slot 2n+2
