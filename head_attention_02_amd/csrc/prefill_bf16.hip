@@ -290,14 +290,18 @@ struct Prefill {
         const bool full = FULL || (all_rows_valid && kbase >= inter_lo && kbase + kBN - 1 <= inter_hi);
         if (!full) {
             keep_branch();
+            // key jj is kept iff lo <= jj <= hi, tested as one unsigned compare
+            // (jj - lo) <= (hi - lo): no scalar mask arithmetic between the compares
             const int lo = lo_r - kbase - 4 * g, hi = hi_r - kbase - 4 * g;
+            const int lo2 = hi >= lo ? lo : (1 << 30);        // empty interval: nothing kept
+            const unsigned span = hi >= lo ? (unsigned)(hi - lo) : 0u;
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int jj = 32 * kb2 + 8 * (e / 4) + (e % 4);
                     if (!POS_SCALE) s[kb2][e] *= c2;
-                    s[kb2][e] = (jj >= lo && jj <= hi) ? s[kb2][e] : kNegInf;
+                    s[kb2][e] = ((unsigned)(jj - lo2) <= span) ? s[kb2][e] : kNegInf;
                 }
         } else if (!POS_SCALE) {
 #pragma unroll
