@@ -30,6 +30,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSteps = 8;   // wave loads per batch (rows per lane group between softmax updates)
+constexpr float kRescaleSlack = 8.0f;   // log2 units the stale running max may lag behind
 
 // Eight consecutive elements as fp32.  STREAM marks a load of cache rows, which are read
 // exactly once: it is issued non-temporal, so the rows stream through the caches without
@@ -169,13 +170,19 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
             copy8<FMT>(a.v_new, new_row, (void*)vc, head_base + (size_t)pos * D + c * 8);
         }
     }
-    for (int base = s0; base < s1; base += BATCH) {
+    // One batch of kSteps wave loads per lane group.  TAIL: the batch reaches past the end
+    // of the key range, so rows are clamped to a valid one and masked; full batches (all
+    // but the last) skip both.  The running max is moved lazily, only when a batch's max
+    // exceeds it by more than 2^8 (p <= 256 otherwise; o and l share the stale max, so
+    // the merge below and the combine pass are unchanged).
+    auto batch = [&](int base, auto tail_c) {
+        constexpr bool TAIL = decltype(tail_c)::value;
         int key[kSteps];
         float kx[kSteps][8];
 #pragma unroll
         for (int u = 0; u < kSteps; ++u) {
             key[u] = base + (u * kWaves + wave) * RPW + r;
-            const int kr = key[u] < s1 ? key[u] : s0;     // out-of-range rows read a valid row
+            const int kr = !TAIL || key[u] < s1 ? key[u] : s0;     // out-of-range rows read a valid row
             if constexpr (MODE == kAppend) {
                 const bool nw = kr == pos;
                 load8<FMT, true>(nw ? a.k_new : kc, nw ? new_row : head_base + (size_t)kr * D + c * 8, kx[u]);
@@ -192,13 +199,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) d = fmaf(qf[t][i], kx[u][i], d);
                 d = row_sum<LPR>(d);
-                s[u][t] = key[u] < s1 ? d : kNegInf;
+                s[u][t] = !TAIL || key[u] < s1 ? d : kNegInf;
             }
         }
         float vx[kSteps][8];
 #pragma unroll
         for (int u = 0; u < kSteps; ++u) {
-            const int kr = key[u] < s1 ? key[u] : s0;
+            const int kr = !TAIL || key[u] < s1 ? key[u] : s0;
             if constexpr (MODE == kAppend) {
                 const bool nw = kr == pos;
                 load8<FMT, true>(nw ? a.v_new : vc, nw ? new_row : head_base + (size_t)kr * D + c * 8, vx[u]);
@@ -206,18 +213,31 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
                 load8<FMT, true>(vc, head_base + (size_t)kr * D + c * 8, vx[u]);
             }
         }
+        float m_new[GT];
+        bool need_any = false;
 #pragma unroll
         for (int t = 0; t < GT; ++t) {
             float mx = kNegInf;
 #pragma unroll
             for (int u = 0; u < kSteps; ++u) mx = fmaxf(mx, s[u][t]);
-            const float m_new = fmaxf(m[t], mx);
-            const float m_use = m_new == kNegInf ? 0.0f : m_new;
-            const float alpha = fast_exp2(m[t] - m_use);
-            m[t] = m_new;
-            float ps = 0.0f;
+            m_new[t] = fmaxf(m[t], mx);
+            need_any |= m_new[t] > m[t] + kRescaleSlack;
+        }
+        if (__builtin_amdgcn_ballot_w64(need_any)) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[t][i] *= alpha;
+            for (int t = 0; t < GT; ++t) {
+                const bool need = m_new[t] > m[t] + kRescaleSlack;
+                const float alpha = need ? fast_exp2(m[t] - m_new[t]) : 1.0f;
+                m[t] = need ? m_new[t] : m[t];
+                l[t] *= alpha;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[t][i] *= alpha;
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < GT; ++t) {
+            const float m_use = m[t] == kNegInf ? 0.0f : m[t];
+            float ps = 0.0f;
 #pragma unroll
             for (int u = 0; u < kSteps; ++u) {
                 const float p = fast_exp2(s[u][t] - m_use);
@@ -225,9 +245,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) o[t][i] = fmaf(p, vx[u][i], o[t][i]);
             }
-            l[t] = l[t] * alpha + ps;
+            l[t] += ps;
         }
-    }
+    };
+    int base = s0;
+    for (; base + BATCH <= s1; base += BATCH) batch(base, std::integral_constant<bool, false>{});
+    if (base < s1) batch(base, std::integral_constant<bool, true>{});
 
     // merge the workgroup's row streams
 #pragma unroll
