@@ -170,9 +170,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
             copy8<FMT>(a.v_new, new_row, (void*)vc, head_base + (size_t)pos * D + c * 8);
         }
     }
-    // One batch of kSteps wave loads per lane group.  TAIL: the batch reaches past the end
-    // of the key range, so rows are clamped to a valid one and masked; full batches (all
-    // but the last) skip both.  The running max is moved lazily, only when a batch's max
+    // One batch of kSteps wave loads per lane group.  TAIL: the last batch of the key range;
+    // it may reach past the end, so its rows are clamped to a valid one and masked, and it
+    // holds the query position, the only row an append takes from the new token (key
+    // s1 - 1 when this split holds the position).  The other batches skip all three.  The running max is moved lazily, only when a batch's max
     // exceeds it by more than 2^8 (p <= 256 otherwise; o and l share the stale max, so
     // the merge below and the combine pass are unchanged).
     auto batch = [&](int base, auto tail_c) {
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         for (int u = 0; u < kSteps; ++u) {
             key[u] = base + (u * kWaves + wave) * RPW + r;
             const int kr = !TAIL || key[u] < s1 ? key[u] : s0;     // out-of-range rows read a valid row
-            if constexpr (MODE == kAppend) {
+            if constexpr (MODE == kAppend && TAIL) {
                 const bool nw = kr == pos;
                 load8<FMT, true>(nw ? a.k_new : kc, nw ? new_row : head_base + (size_t)kr * D + c * 8, kx[u]);
             } else {
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int u = 0; u < kSteps; ++u) {
             const int kr = !TAIL || key[u] < s1 ? key[u] : s0;
-            if constexpr (MODE == kAppend) {
+            if constexpr (MODE == kAppend && TAIL) {
                 const bool nw = kr == pos;
                 load8<FMT, true>(nw ? a.v_new : vc, nw ? new_row : head_base + (size_t)kr * D + c * 8, vx[u]);
             } else {
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         }
     };
     int base = s0;
-    for (; base + BATCH <= s1; base += BATCH) batch(base, std::integral_constant<bool, false>{});
+    for (; base + BATCH < s1; base += BATCH) batch(base, std::integral_constant<bool, false>{});
     if (base < s1) batch(base, std::integral_constant<bool, true>{});
 
     // merge the workgroup's row streams
