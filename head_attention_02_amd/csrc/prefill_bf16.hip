@@ -81,6 +81,7 @@ struct Geo {
     static constexpr int K_BYTES = kBN * D * 2;
     static constexpr int V_BYTES = kBN * D * 2;
     static_assert(NV % kCopyWaves == 0, "V copy rounds cover whole rows");
+    static_assert(NK % kCopyWaves == 0, "every copying wave issues the same number of K copies");
 };
 
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
@@ -130,6 +131,8 @@ struct Prefill {
     uint32_t k_lds0, v_lds0;    // LDS byte addresses of buffer 0
     uint32_t k_off;             // byte offset of this lane's K copy chunk from a copy's base
     uint32_t v_off;             // ... V
+    uint32_t k_cb[G::NKW];      // byte offset of this wave's K copy ii from the tile base (uniform)
+    uint32_t v_cb[G::NVW];      // ... V
     int lo_r, hi_r;             // this lane's key interval
     bool all_rows_valid;
     int inter_lo, inter_hi;     // keys every row of the wave sees
@@ -150,23 +153,22 @@ struct Prefill {
     // offset ((p%32)*D + 8*(p/32))*2 plus a per-copy base (32*kb2*D + 16*kc)*2.
     __device__ __forceinline__ void copy_k(int kt, int par) const {
         const char* base = kg + (size_t)kt * kBN * kv_rs * 2;
-        const bool tail = kt * kBN + kBN > kvalid;
+        const uint32_t lds = k_lds0 + par * G::K_BYTES + cw * 1024;
+        if (kt * kBN + kBN <= kvalid) {   // the whole tile is valid: per-copy bases precomputed
 #pragma unroll
-        for (int ii = 0; ii < G::NKW; ++ii) {
-            const int f = cw + kCopyWaves * ii;
-            if (f < G::NK) {
+            for (int ii = 0; ii < G::NKW; ++ii) lds_dma16(base + k_cb[ii], k_off, lds + kCopyWaves * ii * 1024);
+        } else {
+            keep_branch();
+#pragma unroll
+            for (int ii = 0; ii < G::NKW; ++ii) {
+                const int f = cw + kCopyWaves * ii;
                 const int kb2 = f / G::KC, kc = f % G::KC;
-                const char* b = base + ((size_t)32 * kb2 * kv_rs + 16 * kc) * 2;
-                uint32_t off = k_off;
-                if (tail) {
-                    // keys past the valid length repeat the last valid key; the clamped key
-                    // can lie before this block, so address from the tile base (kt < the
-                    // tile count guarantees kvalid - 1 - kt*64 >= 0)
-                    const int row = min(32 * kb2 + (lane & 31), kvalid - 1 - kt * kBN);
-                    b = base;
-                    off = (uint32_t)((row * kv_rs + 16 * kc + 8 * (lane >> 5)) * 2);
-                }
-                lds_dma16(b, off, k_lds0 + par * G::K_BYTES + f * 1024);
+                // keys past the valid length repeat the last valid key; the clamped key can
+                // lie before this block, so address from the tile base (kt < the tile count
+                // guarantees kvalid - 1 - kt*64 >= 0)
+                const int row = min(32 * kb2 + (lane & 31), kvalid - 1 - kt * kBN);
+                const uint32_t off = (uint32_t)((row * kv_rs + 16 * kc + 8 * (lane >> 5)) * 2);
+                lds_dma16(base, off, lds + kCopyWaves * ii * 1024);
             }
         }
     }
@@ -180,22 +182,21 @@ struct Prefill {
     // offset plus a per-copy base (16c4*D + 32db)*2.
     __device__ __forceinline__ void copy_v(int kt, int par) const {
         const char* base = vg + (size_t)kt * kBN * kv_rs * 2;
-        const bool tail = kt * kBN + kBN > kvalid;
+        const uint32_t lds = v_lds0 + par * G::V_BYTES + cw * 1024;
+        if (kt * kBN + kBN <= kvalid) {
 #pragma unroll
-        for (int ii = 0; ii < G::NVW; ++ii) {
-            const int j = cw + kCopyWaves * ii;
-            if (j < G::NV) {
+            for (int ii = 0; ii < G::NVW; ++ii) lds_dma16(base + v_cb[ii], v_off, lds + kCopyWaves * ii * 1024);
+        } else {
+            keep_branch();
+#pragma unroll
+            for (int ii = 0; ii < G::NVW; ++ii) {   // as for K: clamp, and address from the tile base
+                const int j = cw + kCopyWaves * ii;
                 const int c4 = j / G::DB, db = j % G::DB;
-                const char* b = base + ((size_t)16 * c4 * kv_rs + 32 * db) * 2;
-                uint32_t off = v_off;
-                if (tail) {   // as for K: clamp, and address from the tile base
-                    const int q = lane & 31;
-                    const int r = 8 * (lane >> 5) + 4 * (q >> 4) + ((q & 7) >> 1);
-                    const int row = min(16 * c4 + r, kvalid - 1 - kt * kBN);
-                    b = base;
-                    off = (uint32_t)((row * kv_rs + 32 * db + 16 * ((q >> 3) & 1) + 8 * (q & 1)) * 2);
-                }
-                lds_dma16(b, off, v_lds0 + par * G::V_BYTES + j * 1024);
+                const int q = lane & 31;
+                const int r = 8 * (lane >> 5) + 4 * (q >> 4) + ((q & 7) >> 1);
+                const int row = min(16 * c4 + r, kvalid - 1 - kt * kBN);
+                const uint32_t off = (uint32_t)((row * kv_rs + 32 * db + 16 * ((q >> 3) & 1) + 8 * (q & 1)) * 2);
+                lds_dma16(base, off, lds + kCopyWaves * ii * 1024);
             }
         }
     }
@@ -510,6 +511,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     st.k_lds0 = lds_addr(k_lds[0]);
     st.v_lds0 = lds_addr(v_lds[0]);
     st.k_off = (uint32_t)(((lane & 31) * ir.kv_rs + 8 * (lane >> 5)) * 2);
+#pragma unroll
+    for (int ii = 0; ii < G::NKW; ++ii) {
+        const int f = st.cw + kCopyWaves * ii, kb2 = f / G::KC, kc = f % G::KC;
+        st.k_cb[ii] = (uint32_t)((32 * kb2 * ir.kv_rs + 16 * kc) * 2);
+    }
+#pragma unroll
+    for (int ii = 0; ii < G::NVW; ++ii) {
+        const int j = st.cw + kCopyWaves * ii, c4 = j / G::DB, db = j % G::DB;
+        st.v_cb[ii] = (uint32_t)((16 * c4 * ir.kv_rs + 32 * db) * 2);
+    }
     {
         const int q = lane & 31;
         const int r = 8 * (lane >> 5) + 4 * (q >> 4) + ((q & 7) >> 1);
