@@ -119,7 +119,8 @@ struct Prefill {
     const char* vg;
     uint32_t k_lds0, v_lds0;    // LDS byte addresses of buffer 0
     uint32_t koff[G::NKW];      // byte offsets of this lane's K copy chunks inside a tile
-    uint32_t voff;              // ... V (first copy; the others are +4096 bytes each)
+    uint32_t voff;              // ... V (first copy; copy ii reads v_step * ii bytes further)
+    size_t v_step;              // byte distance between the rows of consecutive V copies
     int k_read;                 // LDS byte offset of this lane's K operand (row l%32, chunk g)
     int v_read[G::DB];          // LDS byte offsets of this lane's transposing V reads
     int lo_r[RB], hi_r[RB];     // this lane's key interval, per row block
@@ -133,45 +134,50 @@ struct Prefill {
     f32x16 o[RB][G::DB];
     float m_run[RB], l_run[RB];
 
+    // Tile copies.  The tail case (rows past the valid length repeat the last valid row)
+    // is decided once per tile; whole tiles use the precomputed per-lane offsets.
     __device__ __forceinline__ void copy_k(int kt, int par) {
         const char* base = kg + (size_t)kt * kBN * kv_rs * 2;
-        const bool tail = kt * kBN + kBN > kvalid;
+        const uint32_t lds = k_lds0 + par * G::K_BYTES + wave * 1024;
+        if (kt * kBN + kBN <= kvalid) {
 #pragma unroll
-        for (int ii = 0; ii < G::NKW; ++ii) {
-            const int i = wave + W * ii;
-            if (i < G::NK) {
-                uint32_t off = koff[ii];
-                if (tail) {   // rows past the valid length repeat the last valid row
+            for (int ii = 0; ii < G::NKW; ++ii)
+                if (G::NK % W == 0 || ii + 1 < G::NKW || wave + W * ii < G::NK)
+                    lds_dma16(base, koff[ii], lds + W * ii * 1024);
+        } else {
+            keep_branch();
+#pragma unroll
+            for (int ii = 0; ii < G::NKW; ++ii) {
+                const int i = wave + W * ii;
+                if (i < G::NK) {
                     const int p = i * 64 + lane;
                     int row = p / G::KS, c = p - (p / G::KS) * G::KS;
                     c = c < G::CPR ? c : 0;
                     row = min(row, kvalid - 1 - kt * kBN);
-                    off = (uint32_t)((row * kv_rs + c * 8) * 2);
+                    lds_dma16(base, (uint32_t)((row * kv_rs + c * 8) * 2), lds + W * ii * 1024);
                 }
-                lds_dma16(base, off, k_lds0 + par * G::K_BYTES + i * 1024);
             }
         }
     }
 
     __device__ __forceinline__ void copy_v(int kt, int par) {
         const char* base = vg + (size_t)kt * kBN * kv_rs * 2;
-        const bool tail = kt * kBN + kBN > kvalid;
-#pragma unroll
-        for (int ii = 0; ii < G::NVW; ++ii) {
-            const int i = wave + W * ii;
-            uint32_t off = voff;
+        const uint32_t lds = v_lds0 + par * G::V_BYTES + wave * 1024;
+        if (kt * kBN + kBN <= kvalid) {
             // copy ii covers the rows W*64/CPR further down than copy ii-1 (same lane
             // offsets: the swizzle repeats with that period)
-            const char* b = base + (size_t)ii * (W * 64 / G::CPR) * kv_rs * 2;
-            if (tail) {
-                const int p = i * 64 + lane;
+#pragma unroll
+            for (int ii = 0; ii < G::NVW; ++ii) lds_dma16(base + ii * v_step, voff, lds + W * ii * 1024);
+        } else {
+            keep_branch();
+#pragma unroll
+            for (int ii = 0; ii < G::NVW; ++ii) {
+                const int p = (wave + W * ii) * 64 + lane;
                 int row = p / G::CPR;
                 const int c = (p % G::CPR) ^ vswz<D>(row);
                 row = min(row, kvalid - 1 - kt * kBN);
-                off = (uint32_t)((row * kv_rs + c * 8) * 2);
-                b = base;
+                lds_dma16(base, (uint32_t)((row * kv_rs + c * 8) * 2), lds + W * ii * 1024);
             }
-            lds_dma16(b, off, v_lds0 + par * G::V_BYTES + i * 1024);
         }
     }
 
@@ -422,6 +428,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __builtin_assume(wave >= 0 && wave < W);
     const int g = lane >> 5;                  // half of the wave
     st.lane = lane;
     st.wave = wave;
@@ -571,6 +578,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
         const int row = p / G::CPR;
         const int c = (p % G::CPR) ^ vswz<D>(row);
         st.voff = (uint32_t)((row * ir.kv_rs + c * 8) * 2);
+        st.v_step = (size_t)(W * 64 / G::CPR) * ir.kv_rs * 2;
     }
     st.k_read = ((lane & 31) * G::KS + g) * 16;
     {
