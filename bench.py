@@ -15,7 +15,9 @@ the stream the kernels run on.  `--workload` benchmarks one other named workload
 
 `--workload copy_calibration` runs a plain 1 GiB device copy instead, the known-size
 reference against which the rocprofv3 FETCH_SIZE / WRITE_SIZE counters are scaled;
-`--record-traffic DIR` (no GPU) turns those counter runs into profiles/traffic.json.
+`--record-traffic DIR` (no GPU) turns those counter runs into profiles/traffic.json, and
+`--record-mfma DIR` (no GPU) turns one matrix-core counter run per prefill workload into
+profiles/mfma.json (clock, MFMA busy share, executed against algorithmic FLOPs).
 """
 from __future__ import annotations
 
@@ -341,6 +343,78 @@ def record_traffic(run_root: Path) -> dict:
 
 
 # ---------------------------------------------------------------------------
+# Matrix-core use from rocprofv3 counter runs -> profiles/mfma.json
+
+# (workload, kernel-name prefix, kernel sources); one --pmc run each, under DIR/<workload>
+MFMA_RUNS = [
+    ("causal_gqa_s4096", "prefill_bf16_kernel<128", ["prefill_bf16.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]),
+    ("causal_gqa_s4096_f16", "prefill_bf16_kernel<128", ["prefill_bf16.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]),
+    ("banded_w128_s8192", "prefill_bf16_narrow_kernel<64",
+     ["prefill_bf16_narrow.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]),
+    ("bert_base_padded", "prefill_bf16_narrow_kernel<64",
+     ["prefill_bf16_narrow.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]),
+    ("bert_base_varlen", "prefill_bf16_narrow_kernel<64",
+     ["prefill_bf16_narrow.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]),
+]
+MFMA_COUNTERS = ["GRBM_GUI_ACTIVE", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU"]
+XCDS, SIMDS = 8, 256 * 4            # MI355X: 8 XCDs, 256 CUs of 4 SIMDs
+MFMA_FLOP_PER_SIMD_CYCLE = 1024     # 16-bit dense: 32x32x16 MFMA (32768 FLOP) per 32 cycles
+
+
+def _per_dispatch_with_time(run_dir: Path, prefix: str) -> dict:
+    """Mean counter values and mean duration (us) over the dispatches whose name has prefix."""
+    import csv
+    files = sorted(run_dir.rglob("*counter_collection.csv"))
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    vals: dict = {}
+    durs: dict = {}
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                if prefix not in r["Kernel_Name"]:
+                    continue
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                durs[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    if not durs:
+        raise ValueError(f"no dispatch of {prefix} under {run_dir}")
+    out = {k: float(np.mean(v)) for k, v in vals.items()}
+    out["duration_us"] = float(np.mean(list(durs.values())))
+    out["dispatches"] = len(durs)
+    return out
+
+
+def record_mfma(run_root: Path) -> dict:
+    """Reads one rocprofv3 --pmc run of MFMA_COUNTERS per workload of MFMA_RUNS (directory
+    <run_root>/<workload>) and writes profiles/mfma.json: per launch, the shader clock
+    (GRBM_GUI_ACTIVE counts the cycles of all 8 XCDs), the share of each SIMD's cycles its
+    matrix core was busy (SQ_VALU_MFMA_BUSY_CYCLES sums the 1024 SIMDs), VALU instructions
+    per SIMD, the MFMA FLOPs executed (busy cycles x 1024 FLOP) against the algorithmic
+    FLOPs, and the algorithmic rate against the 16-bit dense peak."""
+    out = {"_counters": MFMA_COUNTERS, "_simds": SIMDS, "_xcds": XCDS,
+           "_flop_per_busy_cycle": MFMA_FLOP_PER_SIMD_CYCLE, "_peak_TFLOPs": PEAK_BF16_TFLOPS}
+    for name, prefix, src in MFMA_RUNS:
+        w = W.WORKLOADS[name]
+        seq_lens = W.make_inputs(w)["seq_lens"] if w.seq_len_range is not None else None
+        c = _per_dispatch_with_time(run_root / name, prefix)
+        us = c["duration_us"]
+        cyc = c["GRBM_GUI_ACTIVE"] / XCDS
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / SIMDS
+        executed = busy * SIMDS * MFMA_FLOP_PER_SIMD_CYCLE
+        alg = prefill_flops(w, seq_lens)
+        out[name] = {"source_digest": kernel_sources_digest(src), "kernel": prefix,
+                     "dispatches": c["dispatches"], "duration_us": us, "clock_GHz": cyc / (us * 1e3),
+                     "cycles": cyc, "mfma_busy_cycles_per_simd": busy, "mfma_busy_frac": busy / cyc,
+                     "valu_insts_per_simd": c["SQ_ACTIVE_INST_VALU"] / SIMDS,
+                     "executed_mfma_flop": executed, "algorithmic_flop": alg,
+                     "executed_over_algorithmic": executed / alg,
+                     "algorithmic_TFLOPs": alg / (us * 1e-6) / 1e12,
+                     "frac_of_peak": alg / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS}
+    (PROFILES / "mfma.json").write_text(json.dumps(out, indent=1) + "\n")
+    return out
+
+
+# ---------------------------------------------------------------------------
 
 
 def main() -> int:
@@ -356,7 +430,13 @@ def main() -> int:
     ap.add_argument("--record-traffic", metavar="DIR",
                     help="no GPU run: turn the rocprofv3 FETCH_SIZE / WRITE_SIZE runs under DIR into "
                          "profiles/traffic.json")
+    ap.add_argument("--record-mfma", metavar="DIR",
+                    help="no GPU run: turn the rocprofv3 matrix-core counter runs under DIR into "
+                         "profiles/mfma.json")
     args = ap.parse_args()
+    if args.record_mfma:
+        print(json.dumps(record_mfma(Path(args.record_mfma)), indent=1))
+        return 0
     if args.record_traffic:
         print(json.dumps(record_traffic(Path(args.record_traffic)), indent=1))
         return 0
