@@ -170,6 +170,18 @@ def traffic_from_profiles(key: str, digest: str):
     return rec.get("bytes_per_launch")
 
 
+def mfma_from_profiles(key: str, digest: str):
+    """Matrix-core counters of a prefill launch (profiles/mfma.json): clock, busy share and
+    executed / algorithmic FLOPs, or None when the kernel source changed since."""
+    f = PROFILES / "mfma.json"
+    if not f.exists():
+        return None
+    rec = json.loads(f.read_text()).get(key)
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return {k: rec[k] for k in ("clock_GHz", "mfma_busy_frac", "executed_over_algorithmic")}
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle, timed on the host cores on a bounded sample
 
@@ -513,7 +525,8 @@ def main() -> int:
                                  "traffic": traffic_from_profiles(w.name, kernel_sources_digest(src)),
                                  "kernel_ms": ms, **sp, "algorithmic_flop": fl,
                                  "algorithmic_bytes": prefill_bytes(w, x["seq_lens"]),
-                                 "hbm_GBps": prefill_bytes(w, x["seq_lens"]) / sec / 1e9}
+                                 "hbm_GBps": prefill_bytes(w, x["seq_lens"]) / sec / 1e9,
+                                 "mfma_counters": mfma_from_profiles(w.name, kernel_sources_digest(src))}
         else:
             by = decode_bytes(w)
             src = ["decode.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]

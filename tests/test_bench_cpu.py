@@ -128,3 +128,18 @@ def test_more_than_one_gpu_is_refused(capsys, monkeypatch):
     monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2"])
     assert bench.main() == 2
     assert "one GPU" in json.loads(capsys.readouterr().out)["error"]
+
+
+def test_counter_records_follow_the_kernel_source(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", tmp_path)
+    rec = {"source_digest": "abc", "clock_GHz": 2.0, "mfma_busy_frac": 0.5, "executed_over_algorithmic": 1.1,
+           "bytes_per_launch": 7.0}
+    (tmp_path / "mfma.json").write_text(json.dumps({"w": rec}))
+    (tmp_path / "traffic.json").write_text(json.dumps({"w": rec}))
+    assert bench.mfma_from_profiles("w", "abc") == {"clock_GHz": 2.0, "mfma_busy_frac": 0.5,
+                                                     "executed_over_algorithmic": 1.1}
+    assert bench.traffic_from_profiles("w", "abc") == 7.0
+    # a changed kernel source, or an unknown workload: no figure
+    assert bench.mfma_from_profiles("w", "abd") is None
+    assert bench.traffic_from_profiles("w", "abd") is None
+    assert bench.mfma_from_profiles("x", "abc") is None
