@@ -63,6 +63,9 @@ struct Fmt16 {
         else
             return pack_bf16x2(lo, hi);
     }
+    // the two values of a packed pair, widened exactly to fp32
+    __device__ static __forceinline__ float lo(uint32_t w) { return F16 ? f16_lo(w) : bf16_lo(w); }
+    __device__ static __forceinline__ float hi(uint32_t w) { return F16 ? f16_hi(w) : bf16_hi(w); }
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -37,8 +37,12 @@
 // same sequence one phase apart, with a workgroup barrier after every phase, so each
 // SIMD always has one wave on the matrix core and one on the vector ALU.
 //
-// Softmax bookkeeping per tile, for scale > 0: the max is taken over raw scores and the
-// scale is folded into one FMA per score, p = exp2(s*c - m*c) with c = scale*log2(e).
+// Softmax bookkeeping per tile, for scale > 0, with c = scale*log2(e): bf16 Q is
+// multiplied by c once, as it is loaded (and rounded to bf16 again), and each tile's Q.K^T
+// accumulators start from minus the running max m, so the MFMAs leave s*c - m, the
+// exponent of p = exp2(s*c - m) itself, and the vector phase spends no instruction per
+// score on the scale.  (fp16 Q keeps the unscaled form, p = exp2(fma(s, c, -m)): q*c can
+// overflow fp16's range where the fp32 product does not.)
 // The running max is only moved (and O, l rescaled) when the tile's max exceeds it by
 // more than 2^8; otherwise the stale max is kept, p <= 256, and the final O / l is
 // unchanged because numerator and denominator share it.
@@ -120,6 +124,8 @@ template <int D, bool POS_SCALE, bool F16>
 struct Prefill {
     using G = Geo<D>;
     using H = Fmt16<F16>;
+    // bf16 with a positive scale: Q carries the scale and the accumulators the running max
+    static constexpr bool FOLD = POS_SCALE && !F16;
 
     // ---- per-lane constants ---------------------------------------------------------
     int lane, wave, g;
@@ -239,6 +245,8 @@ struct Prefill {
             // step f works on block kb2 = f%2, k-step kc = f/2: consecutive MFMAs alternate
             // between the two accumulation chains
             auto blk = [](int f) { return (f % 2) * G::KC + f / 2; };
+            f32x16 c0 = {};   // FOLD: minus the running max (0 before any key was seen)
+            if constexpr (FOLD) c0 -= (m_run == kNegInf ? 0.0f : m_run);
 #pragma unroll
             for (int f = 0; f < PF; ++f) kf[f] = k_frag(kbuf, blk(f));
 #pragma unroll
@@ -246,7 +254,7 @@ struct Prefill {
                 const int kb2 = f % 2, kc = f / 2;
                 const bf16x8 k_now = kf[f % PF];
                 if (f + PF < NF) kf[f % PF] = k_frag(kbuf, blk(f + PF));
-                s[kb2] = H::mfma32x32x16(k_now, qf[kc], kc == 0 ? f32x16{} : s[kb2]);
+                s[kb2] = H::mfma32x32x16(k_now, qf[kc], kc == 0 ? c0 : s[kb2]);
                 __builtin_amdgcn_sched_barrier(0);   // keep the reads PF steps ahead, no further
             }
         }
@@ -315,11 +323,19 @@ struct Prefill {
 #pragma unroll
             for (int e = 0; e < 16; e += 2) mx = max3(mx, s[kb2][e], s[kb2][e + 1]);
         mx = halves_max(mx);
-        const float m_tile = POS_SCALE ? mx * c2 : mx;
+        // FOLD: the scores are already s*c - m_ref, with m_ref what the accumulators
+        // started from (m_run has not moved since this tile's Q.K^T)
+        const float m_ref = m_run == kNegInf ? 0.0f : m_run;
+        const float m_tile = FOLD ? m_ref + mx : POS_SCALE ? mx * c2 : mx;
         const bool need = m_tile > m_run + kRescaleSlack;
         if (__builtin_amdgcn_ballot_w64(need)) {
             keep_branch();
             const float alpha = need ? fast_exp2(m_run - m_tile) : 1.0f;
+            if constexpr (FOLD) {   // re-reference this tile's exponents to the new max
+                const float d = need ? m_tile - m_ref : 0.0f;
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] -= d;
+            }
             m_run = need ? m_tile : m_run;
             l_run *= alpha;
 #pragma unroll
@@ -334,8 +350,8 @@ struct Prefill {
 #pragma unroll
             for (int jj = 0; jj < 8; jj += 2) {
                 const float s0 = s[c4 / 2][8 * (c4 % 2) + jj], s1 = s[c4 / 2][8 * (c4 % 2) + jj + 1];
-                const float p0 = POS_SCALE ? fast_exp2(fmaf(s0, c2, -m_use)) : fast_exp2(s0 - m_use);
-                const float p1 = POS_SCALE ? fast_exp2(fmaf(s1, c2, -m_use)) : fast_exp2(s1 - m_use);
+                const float p0 = FOLD ? fast_exp2(s0) : POS_SCALE ? fast_exp2(fmaf(s0, c2, -m_use)) : fast_exp2(s0 - m_use);
+                const float p1 = FOLD ? fast_exp2(s1) : POS_SCALE ? fast_exp2(fmaf(s1, c2, -m_use)) : fast_exp2(s1 - m_use);
                 w[jj / 2] = H::pack2(p0, p1);
                 ls0 += p0;
                 ls1 += p1;
@@ -498,6 +514,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
         for (int kc = 0; kc < G::KC; ++kc) {
             u32x4 w = in ? *(const u32x4*)(qrow + 16 * kc + 8 * g) : u32x4{0, 0, 0, 0};
+            if constexpr (Prefill<D, POS_SCALE, F16>::FOLD) {   // c*q, rounded to bf16 (nearest, ties to even)
+                const float c = a.scale * kLog2e;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = H::pack2(H::lo(w[i]) * c, H::hi(w[i]) * c);
+            }
             st.qf[kc] = __builtin_bit_cast(bf16x8, w);
         }
     }
