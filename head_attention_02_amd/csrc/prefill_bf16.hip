@@ -151,6 +151,7 @@ struct Prefill {
     f32x16 s[2];                // scores of the tile the next vector phase works on
     bf16x8 pf[4];               // probabilities of the tile the next matrix phase uses
     float m_run, l_run;
+    f32x16 acc0;                // FOLD: what Q.K^T accumulators start from, -m_run (0 before any key)
 
     // K tile layout in LDS: 1 KiB block f = kb2*KC + kc holds, at 16*p, the chunk 2kc + p/32
     // (dims 16kc + 8(p/32) + [0, 8)) of key 32*kb2 + p%32 -- exactly the MFMA A operand of
@@ -245,8 +246,7 @@ struct Prefill {
             // step f works on block kb2 = f%2, k-step kc = f/2: consecutive MFMAs alternate
             // between the two accumulation chains
             auto blk = [](int f) { return (f % 2) * G::KC + f / 2; };
-            f32x16 c0 = {};   // FOLD: minus the running max (0 before any key was seen)
-            if constexpr (FOLD) c0 -= (m_run == kNegInf ? 0.0f : m_run);
+            const f32x16 c0 = FOLD ? acc0 : f32x16{};
 #pragma unroll
             for (int f = 0; f < PF; ++f) kf[f] = k_frag(kbuf, blk(f));
 #pragma unroll
@@ -337,6 +337,7 @@ struct Prefill {
                 for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] -= d;
             }
             m_run = need ? m_tile : m_run;
+            if constexpr (FOLD) acc0 = f32x16{} - (m_run == kNegInf ? 0.0f : m_run);
             l_run *= alpha;
 #pragma unroll
             for (int i = 0; i < G::DB; ++i) o[i] *= alpha;
@@ -551,6 +552,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
     for (int i = 0; i < G::DB; ++i) st.o[i] = f32x16{};
     st.m_run = kNegInf;    // running (possibly stale) max of this lane's row, log2 units
+    st.acc0 = f32x16{};
     st.l_run = 0.0f;       // running sum over this lane's half of the keys
 
     // ---- the phase sequence ------------------------------------------------------------
