@@ -41,8 +41,9 @@
 // multiplied by c once, as it is loaded (and rounded to bf16 again), and each tile's Q.K^T
 // accumulators start from minus the running max m, so the MFMAs leave s*c - m, the
 // exponent of p = exp2(s*c - m) itself, and the vector phase spends no instruction per
-// score on the scale.  (fp16 Q keeps the unscaled form, p = exp2(fma(s, c, -m)): q*c can
-// overflow fp16's range where the fp32 product does not.)
+// score on the scale.  fp16 Q does the same when c <= 1 (then |c*q| <= |q| stays within
+// fp16's range); with a larger scale it keeps the unscaled form, p = exp2(fma(s, c, -m)),
+// since c*q could overflow fp16 where the fp32 product does not.
 // The running max is only moved (and O, l rescaled) when the tile's max exceeds it by
 // more than 2^8; otherwise the stale max is kept, p <= 256, and the final O / l is
 // unchanged because numerator and denominator share it.
@@ -120,12 +121,14 @@ __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70);
 // keeps it a branch instead of computing its body on every tile and selecting.
 __device__ __forceinline__ void keep_branch() { asm volatile("" ::); }
 
-template <int D, bool POS_SCALE, bool F16>
+// FOLD16: fp16 with c = scale*log2(e) <= 1, where c*q cannot overflow fp16 either.
+template <int D, bool POS_SCALE, bool F16, bool FOLD16>
 struct Prefill {
     using G = Geo<D>;
     using H = Fmt16<F16>;
-    // bf16 with a positive scale: Q carries the scale and the accumulators the running max
-    static constexpr bool FOLD = POS_SCALE && !F16;
+    // Q carries the scale and the accumulators the running max: bf16 with a positive
+    // scale, fp16 when the scale also keeps c*q within fp16's range
+    static constexpr bool FOLD = POS_SCALE && (!F16 || FOLD16);
 
     // ---- per-lane constants ---------------------------------------------------------
     int lane, wave, g;
@@ -364,13 +367,13 @@ struct Prefill {
     }
 };
 
-template <int D, bool POS_SCALE, bool F16>
+template <int D, bool POS_SCALE, bool F16, bool FOLD16>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a) {
     using G = Geo<D>;
     __shared__ __attribute__((aligned(16))) u32x4 k_lds[2][kBN * G::CPR];
     __shared__ __attribute__((aligned(16))) u32x4 v_lds[2][kBN * G::CPR];
 
-    Prefill<D, POS_SCALE, F16> st;
+    Prefill<D, POS_SCALE, F16, FOLD16> st;
     using H = Fmt16<F16>;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -515,7 +518,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
         for (int kc = 0; kc < G::KC; ++kc) {
             u32x4 w = in ? *(const u32x4*)(qrow + 16 * kc + 8 * g) : u32x4{0, 0, 0, 0};
-            if constexpr (Prefill<D, POS_SCALE, F16>::FOLD) {   // c*q, rounded to bf16 (nearest, ties to even)
+            if constexpr (Prefill<D, POS_SCALE, F16, FOLD16>::FOLD) {   // c*q, rounded to 16 bits (nearest, ties to even)
                 const float c = a.scale * kLog2e;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) w[i] = H::pack2(H::lo(w[i]) * c, H::hi(w[i]) * c);
@@ -653,15 +656,19 @@ hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)args.n_qtiles * a.q_heads * a.batch);
     const dim3 block(kThreads);
     if (args.f16) {
-        if (args.scale > 0.0f)
-            hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true>), grid, block, 0, stream, args);
+        // the same float product as the kernel's, so both take the same decision
+        const bool fold16 = args.scale * kLog2e <= 1.0f;
+        if (args.scale > 0.0f && fold16)
+            hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, true>), grid, block, 0, stream, args);
+        else if (args.scale > 0.0f)
+            hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, false>), grid, block, 0, stream, args);
         else
-            hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true>), grid, block, 0, stream, args);
+            hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, false>), grid, block, 0, stream, args);
     } else {
         if (args.scale > 0.0f)
-            hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false>), grid, block, 0, stream, args);
+            hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false, false>), grid, block, 0, stream, args);
         else
-            hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false>), grid, block, 0, stream, args);
+            hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, false>), grid, block, 0, stream, args);
     }
     return hipGetLastError();
 }

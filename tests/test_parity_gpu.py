@@ -155,6 +155,22 @@ def test_prefill_nonpositive_scale(mi, ref, D, scale):
     check(to_f64(got), want, "bf16", f"scale {scale} D {D}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("scale", [0.05, 0.5, 1.0 / math.log2(math.e), 0.75, 2.0])
+def test_prefill_positive_scales(mi, ref, D, dtype, scale):
+    """Positive scales on both sides of scale * log2(e) = 1: below it the fp16 kernels may
+    carry the scale in Q, above it they keep it out (c * q could overflow fp16); bf16
+    carries it at any positive scale."""
+    say(f"prefill scale {scale:.4f} {dtype} D {D}")
+    x = W.random_prefill(17, 1, 4, 2, 230, 230, D, dtype, sigma=0.5)
+    want = ref.prefill(x["q"], x["k"], x["v"], scale=scale, causal=True)
+    got = mi.attn_prefill(to_gpu(x["q"]), to_gpu(x["k"]), to_gpu(x["v"]), causal=True, scale=scale)
+    import torch
+    torch.cuda.synchronize()
+    check(to_f64(got), want, dtype, f"scale {scale:.4f} {dtype} D {D}")
+
+
 # ---------------------------------------------------------------------------
 # edge cases
 
