@@ -656,7 +656,7 @@ hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)args.n_qtiles * a.q_heads * a.batch);
     const dim3 block(kThreads);
     if (args.f16) {
-        // the same float product as the kernel's, so both take the same decision
+        // c as the kernel computes it (one float product): c <= 1 here means |c*q| <= |q| there
         const bool fold16 = args.scale * kLog2e <= 1.0f;
         if (args.scale > 0.0f && fold16)
             hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, true>), grid, block, 0, stream, args);

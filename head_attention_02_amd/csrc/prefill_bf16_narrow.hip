@@ -413,7 +413,7 @@ struct Cfg {
 // GATE: waves skip the work of key tiles none of their rows sees.  Only causal and banded
 // launches have such tiles; the full bidirectional launch keeps the ungated stream, whose
 // schedule the extra branches would only disturb (measured 39.9 vs 41.3 us on the padded
-// BERT batch).
+// BERT batch, both timed in the kernel's form for a non-positive scale).
 template <int D, bool POS_SCALE, bool GATE, bool F16>
 __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_narrow_kernel(PrefillArgs a) {
     constexpr int RB = Cfg<D>::RB;
