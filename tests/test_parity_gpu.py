@@ -171,6 +171,32 @@ def test_prefill_positive_scales(mi, ref, D, dtype, scale):
     check(to_f64(got), want, dtype, f"scale {scale:.4f} {dtype} D {D}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_running_max_keeps_moving(mi, ref, D, dtype, causal):
+    """Scores that grow by about 10 (log2 units) per 64 keys: every row's running max
+    moves past the lazy-rescale slack on nearly every key tile, so the rescale path (O and
+    the row sum scaled down, the tile's exponents re-referenced to the new max) runs
+    tile after tile instead of once."""
+    say(f"prefill growing scores {dtype} D {D} causal {causal}")
+    rng = np.random.default_rng(23)
+    L, scale = 300, 1.0 / math.sqrt(D)
+    u = np.full(D, 1.0 / math.sqrt(D), np.float32)
+    per_key = 10.0 / 64 / (scale * math.log2(math.e))      # score growth per key, before the scale
+    q = 4.0 * u + 0.1 * rng.standard_normal((1, 2, L, D), dtype=np.float32)
+    k = (per_key / 4.0) * np.arange(L, dtype=np.float32)[None, None, :, None] * u \
+        + 0.1 * rng.standard_normal((1, 1, L, D), dtype=np.float32)
+    v = rng.standard_normal((1, 1, L, D), dtype=np.float32)
+    cast = W.bf16_bits_from_f32 if dtype == "bf16" else (lambda a: a.astype(np.float16))
+    q, k, v = cast(q), cast(k), cast(v)
+    want = ref.prefill(q, k, v, scale=scale, causal=causal)
+    got = mi.attn_prefill(to_gpu(q), to_gpu(k), to_gpu(v), causal=causal, scale=scale)
+    import torch
+    torch.cuda.synchronize()
+    check(to_f64(got), want, dtype, f"growing scores {dtype} D {D} causal {causal}")
+
+
 # ---------------------------------------------------------------------------
 # edge cases
 
