@@ -197,6 +197,30 @@ def test_prefill_running_max_keeps_moving(mi, ref, D, dtype, causal):
     check(to_f64(got), want, dtype, f"growing scores {dtype} D {D} causal {causal}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_running_max_keeps_moving(mi, ref, D, dtype):
+    """Decode over a cache whose scores grow by about 10 (log2 units) per 64 positions:
+    each key range's running max keeps moving past the lazy-rescale slack, and the
+    partial states of the ranges differ by orders of magnitude before they are combined."""
+    say(f"decode growing scores {dtype} D {D}")
+    rng = np.random.default_rng(29)
+    B, Hq, Hkv, L, scale = 4, 8, 2, 1000, 1.0 / math.sqrt(D)
+    u = np.full(D, 1.0 / math.sqrt(D), np.float32)
+    per_key = 10.0 / 64 / (scale * math.log2(math.e))
+    q = 4.0 * u + 0.1 * rng.standard_normal((B, Hq, D), dtype=np.float32)
+    k = (per_key / 4.0) * np.arange(L, dtype=np.float32)[None, None, :, None] * u \
+        + 0.1 * rng.standard_normal((B, Hkv, L, D), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, L, D), dtype=np.float32)
+    cast = W.bf16_bits_from_f32 if dtype == "bf16" else (lambda a: a.astype(np.float16))
+    q, k, v = cast(q), cast(k), cast(v)
+    want = ref.decode(q, k, v, kv_len=L, scale=scale, pos_offset=L - 1)
+    got = mi.attn_decode(to_gpu(q), to_gpu(k), to_gpu(v), kv_len=L, pos_offset=L - 1, scale=scale)
+    import torch
+    torch.cuda.synchronize()
+    check(to_f64(got), want, dtype, f"decode growing scores {dtype} D {D}")
+
+
 # ---------------------------------------------------------------------------
 # edge cases
 
