@@ -163,7 +163,7 @@ size_t attn_decode_workspace_bytes(int batch, int q_heads, int kv_heads, int kv_
     if (batch <= 0 || q_heads < 1 || kv_heads < 1 || q_heads % kv_heads || kv_len < 1 ||
         !supported_head_dim(head_dim))
         return 0;
-    const mi_attn::DecodePlan p = mi_attn::plan_decode(batch, q_heads, kv_heads, kv_len, head_dim);
+    const mi_attn::plan::DecodePlan p = mi_attn::plan_decode(batch, q_heads, kv_heads, kv_len, head_dim);
     if (p.splits == 1) return 0;   // one workgroup per key range writes the output itself
     return (size_t)batch * q_heads * p.splits * (head_dim + 2) * sizeof(float);
 }
@@ -206,7 +206,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o
                     need);
     if (!aligned16(workspace)) return fail(MI_ATTN_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
 
-    const mi_attn::DecodePlan p = mi_attn::plan_decode(batch, q_heads, kv_heads, kv_len, head_dim);
+    const mi_attn::plan::DecodePlan p = mi_attn::plan_decode(batch, q_heads, kv_heads, kv_len, head_dim);
     mi_attn::DecodeArgs a{};
     a.q = q;
     a.k = k_cache;
@@ -272,7 +272,7 @@ int decode_per_item(const char* fn, const void* q, const void* const* k_caches, 
                     need);
     if (!aligned16(workspace)) return fail(MI_ATTN_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
 
-    const mi_attn::DecodePlan p = mi_attn::plan_decode(batch, q_heads, kv_heads, capacity, head_dim);
+    const mi_attn::plan::DecodePlan p = mi_attn::plan_decode(batch, q_heads, kv_heads, capacity, head_dim);
     mi_attn::DecodeArgs a{};
     a.q = q;
     a.k_ptrs = k_caches;

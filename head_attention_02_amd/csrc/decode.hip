@@ -27,9 +27,9 @@
 namespace mi_attn {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = plan::DecodeGeo<128>::WAVES;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kSteps = 8;   // wave loads per batch (rows per lane group between softmax updates)
+constexpr int kSteps = plan::DecodeGeo<128>::STEPS;   // wave loads per batch (rows per lane group between softmax updates)
 constexpr float kRescaleSlack = 8.0f;   // log2 units the stale running max may lag behind
 
 // Eight consecutive elements as fp32.  STREAM marks a load of cache rows, which are read
@@ -91,10 +91,10 @@ __device__ __forceinline__ void store1(void* out, size_t at, float v) {
 
 template <int D, int GT, int FMT, int MODE>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
-    constexpr int LPR = D / 8;            // lanes per key row, 8 elements per lane
-    constexpr int RPW = 64 / LPR;         // rows per wave load
-    constexpr int STREAMS = RPW * kWaves; // independent row streams in the workgroup
-    constexpr int BATCH = STREAMS * kSteps;
+    constexpr int LPR = plan::DecodeGeo<D>::LPR;          // lanes per key row, 8 elements per lane
+    constexpr int RPW = plan::DecodeGeo<D>::RPW;          // rows per wave load
+    constexpr int STREAMS = plan::DecodeGeo<D>::STREAMS;  // independent row streams in the workgroup
+    constexpr int BATCH = plan::DecodeGeo<D>::BATCH;
 
     __shared__ float s_m[STREAMS][GT];
     __shared__ float s_l[STREAMS][GT];
@@ -111,26 +111,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     const int group = a.q_heads / a.kv_heads;
     const int h0 = kvh * group + hg * GT;
 
-    // query position and the key interval [lo, hi] it sees
-    int len, pos;
-    if constexpr (MODE == kAppend) {
-        // kv_lens holds the lengths before the append: the new token goes to slot
-        // kv_lens[b] and its query sits there.  No room (a length outside
-        // [0, capacity)): nothing is written and the output is zero.
-        const int cl = a.kv_lens[b];
-        len = (cl >= 0 && cl < a.capacity) ? cl + 1 : 0;
-        pos = len - 1;
-    } else if (a.kv_lens) {
-        len = min(max(a.kv_lens[b], 0), a.kv_len);
-        pos = len - 1;
-    } else {
-        len = a.kv_len;
-        pos = a.pos_offset;
-    }
-    const int lo = a.window > 0 ? max(0, pos - a.window + 1) : 0;
-    const int hi = min(pos, len - 1);
-    const int s0 = max(lo, split * a.split_len);
-    const int s1 = min(hi + 1, (split + 1) * a.split_len);
+    // the query's position and the keys [s0, s1) this split attends (plan::decode_query,
+    // plan::decode_split_keys)
+    const plan::DecodeQuery dq = plan::decode_query(MODE == kAppend, a.kv_lens != nullptr,
+                                                    a.kv_lens ? a.kv_lens[b] : 0, a.kv_len, a.capacity,
+                                                    a.pos_offset);
+    const int pos = dq.pos;
+    const plan::KeyRange kr_split = plan::decode_split_keys(dq, a.window, split, a.split_len);
+    const int s0 = kr_split.s0;
+    const int s1 = kr_split.s1;
 
     // queries of the GT heads, pre-multiplied by scale * log2(e)
     const float c2 = a.scale * kLog2e;
@@ -183,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int u = 0; u < kSteps; ++u) {
             key[u] = base + (u * kWaves + wave) * RPW + r;
-            const int kr = !TAIL || key[u] < s1 ? key[u] : s0;     // out-of-range rows read a valid row
+            const int kr = plan::decode_key_row(key[u], s0, s1, TAIL);   // out-of-range rows read a valid row
             if constexpr (MODE == kAppend && TAIL) {
                 const bool nw = kr == pos;
                 load8<FMT, true>(nw ? a.k_new : kc, nw ? new_row : head_base + (size_t)kr * D + c * 8, kx[u]);
@@ -206,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         float vx[kSteps][8];
 #pragma unroll
         for (int u = 0; u < kSteps; ++u) {
-            const int kr = !TAIL || key[u] < s1 ? key[u] : s0;
+            const int kr = plan::decode_key_row(key[u], s0, s1, TAIL);
             if constexpr (MODE == kAppend && TAIL) {
                 const bool nw = kr == pos;
                 load8<FMT, true>(nw ? a.v_new : vc, nw ? new_row : head_base + (size_t)kr * D + c * 8, vx[u]);
@@ -341,28 +330,13 @@ hipError_t launch_d(const DecodeArgs& a, int gt, hipStream_t stream) {
 
 }  // namespace
 
-DecodePlan plan_decode(int batch, int q_heads, int kv_heads, int kv_len, int head_dim) {
-    DecodePlan p{};
-    const int group = q_heads / kv_heads;
-    p.heads_per_group = group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
-    p.head_groups = group / p.heads_per_group;
-    const long units = (long)batch * kv_heads * p.head_groups;
-    // Two workgroups fit on a CU (the split kernel's register use allows two waves per
-    // SIMD), so 512 workgroups fill MI355X's 256 CUs exactly once.  Splitting further only
-    // shortens the streams and adds partial states: on the batch-64 kv-8192 decode, 512
-    // workgroups (no split) ran in 318 us, 1024 in 324 us, 2048 in 333 us.
-    const long target_wgs = 512;
-    long splits = (target_wgs + units - 1) / units;
-    const long max_splits = (kv_len + 255) / 256;
-    if (splits > max_splits) splits = max_splits;
-    if (splits < 1) splits = 1;
-    long split_len = (kv_len + splits - 1) / splits;
-    split_len = (split_len + 63) / 64 * 64;
-    splits = (kv_len + split_len - 1) / split_len;
-    p.splits = (int)splits;
-    p.split_len = (int)split_len;
+// Two workgroups fit on a CU (the split kernel's register use allows two waves per
+// SIMD), so 512 workgroups fill MI355X's 256 CUs exactly once.  Splitting further only
+// shortens the streams and adds partial states: on the batch-64 kv-8192 decode, 512
+// workgroups (no split) ran in 318 us, 1024 in 324 us, 2048 in 333 us.
+plan::DecodePlan plan_decode(int batch, int q_heads, int kv_heads, int kv_len, int head_dim) {
     (void)head_dim;
-    return p;
+    return plan::decode_plan(batch, q_heads, kv_heads, kv_len, 512);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int heads_per_group, int dtype,

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "tile_plan.hpp"
+
 namespace mi_attn {
 
 // One prefill problem, as validated by attn_prefill or attn_prefill_varlen.
@@ -29,43 +31,15 @@ struct PrefillArgs {
     int token_major;
 };
 
-// Where one (item, query head)'s rows live and how many there are (element offsets and
-// strides; the same code serves both layouts).
-struct ItemRows {
-    size_t q_base;    // row 0 of (item, query head) in q and out
-    size_t kv_base;   // row 0 of (item, kv head) in k and v
-    int q_rs, kv_rs;  // elements from one row to the next
-    int q_len;        // query rows of the item
-    int kv_valid;     // keys of the item (seq_lens applied)
-};
-
-__device__ __forceinline__ ItemRows item_rows(const PrefillArgs& a, int b, int h, int kvh, int D) {
-    ItemRows r;
-    if (a.cu_seqlens) {
-        const int t0 = a.cu_seqlens[b];
-        const int n = min(max(a.cu_seqlens[b + 1] - t0, 0), a.q_len);
-        r.q_rs = a.q_heads * D;
-        r.kv_rs = a.kv_heads * D;
-        r.q_base = (size_t)t0 * r.q_rs + (size_t)h * D;
-        r.kv_base = (size_t)t0 * r.kv_rs + (size_t)kvh * D;
-        r.q_len = n;
-        r.kv_valid = n;
-    } else if (a.token_major) {
-        r.q_rs = a.q_heads * D;
-        r.kv_rs = a.kv_heads * D;
-        r.q_base = (size_t)b * a.q_len * r.q_rs + (size_t)h * D;
-        r.kv_base = (size_t)b * a.kv_len * r.kv_rs + (size_t)kvh * D;
-        r.q_len = a.q_len;
-        r.kv_valid = a.seq_lens ? min(max(a.seq_lens[b], 0), a.kv_len) : a.kv_len;
-    } else {
-        r.q_rs = D;
-        r.kv_rs = D;
-        r.q_base = ((size_t)b * a.q_heads + h) * (size_t)a.q_len * D;
-        r.kv_base = ((size_t)b * a.kv_heads + kvh) * (size_t)a.kv_len * D;
-        r.q_len = a.q_len;
-        r.kv_valid = a.seq_lens ? min(max(a.seq_lens[b], 0), a.kv_len) : a.kv_len;
-    }
-    return r;
+// Where one (item, query head)'s rows live and how many there are: the device side of
+// plan::item_rows, reading the item's token range or valid length.
+__device__ __forceinline__ plan::Rows item_rows(const PrefillArgs& a, int b, int h, int kvh, int D) {
+    if (a.cu_seqlens)
+        return plan::item_rows(plan::kUnpadded, b, h, kvh, D, a.q_heads, a.kv_heads, a.q_len, a.kv_len,
+                               a.cu_seqlens[b], a.cu_seqlens[b + 1], false, 0);
+    const plan::Layout lay = a.token_major ? plan::kTokenMajor : plan::kHeadMajor;
+    return plan::item_rows(lay, b, h, kvh, D, a.q_heads, a.kv_heads, a.q_len, a.kv_len, 0, 0, a.seq_lens != nullptr,
+                           a.seq_lens ? a.seq_lens[b] : 0);
 }
 
 // One decode problem, as validated and planned by attn_decode.
@@ -101,10 +75,8 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, hipStream_t st
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int heads_per_group, int dtype,
                          hipStream_t stream);
 
-// Decode launch plan shared by the call and the workspace query.
-struct DecodePlan {
-    int splits, split_len, heads_per_group, head_groups;
-};
-DecodePlan plan_decode(int batch, int q_heads, int kv_heads, int kv_len, int head_dim);
+// Decode launch plan shared by the call and the workspace query (plan::decode_plan with
+// the grid target the split kernel is tuned for).
+plan::DecodePlan plan_decode(int batch, int q_heads, int kv_heads, int kv_len, int head_dim);
 
 }  // namespace mi_attn

@@ -48,78 +48,27 @@
 // more than 2^8; otherwise the stale max is kept, p <= 256, and the final O / l is
 // unchanged because numerator and denominator share it.
 //
-// LDS layout (bank conflicts): gfx950 LDS has 64 four-byte banks.  One ds_read_b128
-// phase (16 lanes) reads 16 consecutive K rows at one 16-byte chunk, so K rows are
-// padded to D/8+1 chunks.  One ds_read_b64_tr_b16 phase (32 lanes) reads 4 consecutive V
-// rows at one 64-byte column group, so V rows are XOR-swizzled at 64-byte granularity:
-// chunk c of row r sits at chunk c ^ vswz(r), which puts the four rows in four
-// different quarters of the 256 bytes the banks cover.
+// LDS layout: operand-linear 1 KiB blocks, no padding and no swizzle.  Copy f of a K tile
+// places at byte 16*l of block f exactly the 16 bytes lane l's MFMA A operand needs, and
+// copy j of a V tile places what lane l's two transposing reads need at 8*l of two
+// 512-byte blocks (plan::wide_k_chunk, plan::wide_v_chunk).  Every operand read is then
+// one contiguous 1 KiB (or 512-byte) access with no bank conflict.
 #include <type_traits>
 
-#include "mi_attn_device.hpp"
-#include "mi_attn_kernels.hpp"
+#include "prefill_common.hpp"
 
 namespace mi_attn {
 namespace {
 
-constexpr int kBN = 64;                // keys per tile
-constexpr int kWaves = 8;              // two groups of four, one wave of each per SIMD
+constexpr int kBN = plan::WideGeo<128>::BN;            // keys per tile
+constexpr int kWaves = plan::WideGeo<128>::WAVES;       // two groups of four, one wave of each per SIMD
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;       // query rows per workgroup
-constexpr int kCopyWaves = 4;          // the trailing group issues every tile copy
+constexpr int kBM = plan::WideGeo<128>::BM;             // query rows per workgroup
+constexpr int kCopyWaves = plan::WideGeo<128>::COPY_WAVES;   // the trailing group issues every tile copy
 constexpr float kRescaleSlack = 8.0f;  // log2 units the stale max may lag behind
-constexpr int kXcds = 8;               // accelerator complex dies (one L2 each) on MI355X
-
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 template <int D>
-struct Geo {
-    static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-    static constexpr int KC = D / 16;                  // MFMA k-steps of Q.K^T
-    static constexpr int DB = D / 32;                  // 32-wide blocks of the output head dim
-    static constexpr int NK = 2 * KC;                  // K copy instructions per tile (1 KiB each)
-    static constexpr int NKW = (NK + kCopyWaves - 1) / kCopyWaves;
-    static constexpr int NV = 4 * DB;                  // V copy instructions per tile (1 KiB each)
-    static constexpr int NVW = (NV + kCopyWaves - 1) / kCopyWaves;
-    static constexpr int K_BYTES = kBN * D * 2;
-    static constexpr int V_BYTES = kBN * D * 2;
-    static_assert(NV % kCopyWaves == 0, "V copy rounds cover whole rows");
-    static_assert(NK % kCopyWaves == 0, "every copying wave issues the same number of K copies");
-};
-
-__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
-
-// Row max / sum over both halves of the wave (lanes l and l^32 hold the same query row).
-__device__ __forceinline__ float halves_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// One 16-byte-per-lane copy from global memory straight into LDS: lane l reads
-// sbase + voff and its 16 bytes land at LDS address m0 + 16 * l (sbase and m0 are
-// wave-uniform).  Written as inline assembly so that the compiler does not track it as
-// an outstanding LDS write -- it would otherwise wait for every copy in flight
-// (vmcnt(0)), including the next tile's, before each LDS read -- and the kernel's own
-// vmcnt wait and barrier order the copies against the reads.
-__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t m0) {
-    asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(m0));
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
-}
-
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Marks a rarely taken, wave-uniform branch as having a side effect so that the compiler
-// keeps it a branch instead of computing its body on every tile and selecting.
-__device__ __forceinline__ void keep_branch() { asm volatile("" ::); }
+using Geo = plan::WideGeo<D>;
 
 // FOLD16: fp16 with c = scale*log2(e) <= 1, where c*q cannot overflow fp16 either.
 template <int D, bool POS_SCALE, bool F16, bool FOLD16>
@@ -158,9 +107,9 @@ struct Prefill {
 
     // K tile layout in LDS: 1 KiB block f = kb2*KC + kc holds, at 16*p, the chunk 2kc + p/32
     // (dims 16kc + 8(p/32) + [0, 8)) of key 32*kb2 + p%32 -- exactly the MFMA A operand of
-    // lane p, so every K operand read is the lane-linear base + 16*lane.  Copy instruction
-    // f fills block f: lane p reads key 32kb2 + p%32 at chunk 2kc + p/32, i.e. a per-lane
-    // offset ((p%32)*D + 8*(p/32))*2 plus a per-copy base (32*kb2*D + 16*kc)*2.
+    // lane p, so every K operand read is the lane-linear base + 16*lane.  Copy f fills block
+    // f (plan::wide_k_chunk): a per-lane offset plus a per-copy base for whole tiles; tail
+    // tiles clamp their rows to the last valid key, addressed from the tile base.
     __device__ __forceinline__ void copy_k(int kt, int par) const {
         const char* base = kg + (size_t)kt * kBN * kv_rs * 2;
         const uint32_t lds = k_lds0 + par * G::K_BYTES + cw * 1024;
@@ -171,14 +120,9 @@ struct Prefill {
             keep_branch();
 #pragma unroll
             for (int ii = 0; ii < G::NKW; ++ii) {
-                const int f = cw + kCopyWaves * ii;
-                const int kb2 = f / G::KC, kc = f % G::KC;
-                // keys past the valid length repeat the last valid key; the clamped key can
-                // lie before this block, so address from the tile base (kt < the tile count
-                // guarantees kvalid - 1 - kt*64 >= 0)
-                const int row = min(32 * kb2 + (lane & 31), kvalid - 1 - kt * kBN);
-                const uint32_t off = (uint32_t)((row * kv_rs + 16 * kc + 8 * (lane >> 5)) * 2);
-                lds_dma16(base, off, lds + kCopyWaves * ii * 1024);
+                plan::Chunk c = plan::wide_k_chunk(cw + kCopyWaves * ii, lane, G::KC);
+                c.row = plan::tail_row(c.row, kvalid, kt * kBN);
+                lds_dma16(base, plan::chunk_offset(c, kv_rs), lds + kCopyWaves * ii * 1024);
             }
         }
     }
@@ -186,10 +130,8 @@ struct Prefill {
     // V tile layout in LDS: 512-byte block 2j + hi (j = c4*DB + db) holds, at 8*l, what
     // lane l reads in the transposing read of V^T operand j, half hi: key
     // 16c4 + 8hi + 4(l/32) + (l%16)/4, dims 32db + 16((l/16)%2) + 4(l%4) + [0, 4).  So both
-    // transposing reads are the lane-linear base + 8*lane (+512).  Copy instruction j fills
-    // blocks 2j, 2j+1; its 16-byte lane p (hi = p/32, q = p%32) takes key
-    // 16c4 + 8hi + 4(q/16) + (q%8)/2 at dims 32db + 16((q/8)%2) + 8(q%2) -- a per-lane
-    // offset plus a per-copy base (16c4*D + 32db)*2.
+    // transposing reads are the lane-linear base + 8*lane (+512).  Copy j fills blocks 2j,
+    // 2j+1 (plan::wide_v_chunk), addressed like the K copies.
     __device__ __forceinline__ void copy_v(int kt, int par) const {
         const char* base = vg + (size_t)kt * kBN * kv_rs * 2;
         const uint32_t lds = v_lds0 + par * G::V_BYTES + cw * 1024;
@@ -199,14 +141,10 @@ struct Prefill {
         } else {
             keep_branch();
 #pragma unroll
-            for (int ii = 0; ii < G::NVW; ++ii) {   // as for K: clamp, and address from the tile base
-                const int j = cw + kCopyWaves * ii;
-                const int c4 = j / G::DB, db = j % G::DB;
-                const int q = lane & 31;
-                const int r = 8 * (lane >> 5) + 4 * (q >> 4) + ((q & 7) >> 1);
-                const int row = min(16 * c4 + r, kvalid - 1 - kt * kBN);
-                const uint32_t off = (uint32_t)((row * kv_rs + 32 * db + 16 * ((q >> 3) & 1) + 8 * (q & 1)) * 2);
-                lds_dma16(base, off, lds + kCopyWaves * ii * 1024);
+            for (int ii = 0; ii < G::NVW; ++ii) {
+                plan::Chunk c = plan::wide_v_chunk(cw + kCopyWaves * ii, lane, G::DB);
+                c.row = plan::tail_row(c.row, kvalid, kt * kBN);
+                lds_dma16(base, plan::chunk_offset(c, kv_rs), lds + kCopyWaves * ii * 1024);
             }
         }
     }
@@ -384,34 +322,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     st.wave = wave;
     st.g = g;
     st.cw = wave - 4;
-    // One-dimensional grid, q-tile slowest: for causal attention the tiles near the end of
-    // the sequence carry the most keys, so the whole grid runs longest-first and the short
-    // tiles fill in at the end instead of leaving a tail of long ones.
-    // Workgroups are dealt round-robin to the 8 XCDs (block i to XCD i % 8), each with its
-    // own L2.  When the (item, kv head) units divide evenly, every XCD gets whole units --
-    // all query heads of a kv head -- so that a unit's K/V tiles are fetched into one L2
-    // and reused there by all its query heads.
-    const int qgrp = a.q_heads / a.kv_heads;
-    const int units = a.batch * a.kv_heads;
-    int qt_rank, b, h;
-    if (units % kXcds == 0) {
-        const int xcd = (int)(blockIdx.x % kXcds), k = (int)(blockIdx.x / kXcds);
-        const int per_xcd = units / kXcds;
-        const int hig = k % qgrp;
-        const int unit = ((k / qgrp) % per_xcd) * kXcds + xcd;
-        qt_rank = k / (qgrp * per_xcd);
-        b = unit / a.kv_heads;
-        h = (unit % a.kv_heads) * qgrp + hig;
-    } else {
-        const int bh = (int)(blockIdx.x % (unsigned)(a.batch * a.q_heads));
-        qt_rank = (int)(blockIdx.x / (unsigned)(a.batch * a.q_heads));
-        b = bh / a.q_heads;
-        h = bh % a.q_heads;
-    }
-    const int qt = a.causal ? (a.n_qtiles - 1 - qt_rank) : qt_rank;
-    const int kvh = h / qgrp;
+    // block -> (q-tile, item, head): longest causal tiles first, XCD-aware (plan::map_block)
+    const plan::BlockCoord bc = plan::map_block(blockIdx.x, a.n_qtiles, a.batch, a.q_heads, a.kv_heads,
+                                                a.causal != 0, kXcds);
+    const int qt = bc.qt, b = bc.b, h = bc.h;
+    const int kvh = h / (a.q_heads / a.kv_heads);
 
-    const ItemRows ir = item_rows(a, b, h, kvh, D);
+    const plan::Rows ir = item_rows(a, b, h, kvh, D);
     const int valid = ir.kv_valid;
     const int q_len = ir.q_len;
     st.kvalid = valid;
@@ -420,42 +337,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     const int q0 = qt * kBM;
     if (q0 >= q_len) return;   // no query row of this item in the tile (unpadded layout)
     const int last_row = min(q0 + kBM, q_len) - 1;
-    const int half_w = a.window / 2;
 
-    // ---- key range of the whole workgroup -------------------------------------------
+    // ---- key tiles of the whole workgroup, and those every row sees in full -------------
+    const bool causal = a.causal != 0;
     const int p_lo = a.pos_offset + q0;
     const int p_hi = a.pos_offset + last_row;
-    int k_begin = 0;
-    int k_end = valid;
-    if (a.causal) k_end = min(k_end, p_hi + 1);
-    if (a.window > 0) {
-        if (a.causal) {
-            k_begin = max(k_begin, p_lo - a.window + 1);
-        } else {
-            k_begin = max(k_begin, p_lo - half_w);
-            k_end = min(k_end, p_hi + half_w + 1);
-        }
-    }
-    if (p_lo >= valid) k_end = k_begin;       // every row of the tile is padding
-    const int kt_begin = k_begin / kBN;
-    const int kt_end = k_end > k_begin ? (k_end + kBN - 1) / kBN : kt_begin;
-    // Key tiles every row of the workgroup sees in full: [full_lo, full_hi] (keys).
-    int full_lo = 0, full_hi = valid - 1;
-    if (a.causal) full_hi = min(full_hi, p_lo);
-    if (a.window > 0) {
-        if (a.causal) {
-            full_lo = max(0, p_hi - a.window + 1);
-        } else {
-            full_lo = max(0, p_hi - half_w);
-            full_hi = min(full_hi, p_lo + half_w);
-        }
-    }
-    if (p_hi >= valid || q0 + kBM > q_len) full_hi = -1;   // some row is padding or past the end
+    const plan::Tiles tiles = plan::key_tiles(plan::span_union(p_lo, p_hi, valid, causal, a.window), kBN);
+    const int kt_begin = tiles.begin;
+    const int kt_end = tiles.end;
+    plan::Keys full = plan::span_inter(p_lo, p_hi, valid, causal, a.window);
+    if (p_hi >= valid || q0 + kBM > q_len) full.hi = -1;   // some row is padding or past the end
     // the loop runs V(t) on tile kt_begin + t + 1, t in [0, n-1): tiles of t in [ta, tb) are full
     const int nv = max(kt_end - kt_begin - 1, 0);   // vector phases in the loop
     int ta = 0, tb = 0;
-    if (full_hi >= full_lo) {
-        const int f0 = (full_lo + kBN - 1) / kBN, f1 = (full_hi + 1) / kBN;   // full tiles [f0, f1)
+    if (full.hi >= full.lo) {
+        const int f0 = (full.lo + kBN - 1) / kBN, f1 = (full.hi + 1) / kBN;   // full tiles [f0, f1)
         ta = min(max(f0 - kt_begin - 1, 0), nv);
         tb = min(max(f1 - kt_begin - 1, ta), nv);
     }
@@ -466,49 +362,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     const int r0 = q0 + wave * 32;
     const int my_row = r0 + (lane & 31);
     {
-        const int my_pos = a.pos_offset + my_row;
-        int lo_r = 0, hi_r = valid - 1;
-        if (a.causal) hi_r = min(hi_r, my_pos);
-        if (a.window > 0) {
-            if (a.causal) {
-                lo_r = max(0, my_pos - a.window + 1);
-            } else {
-                lo_r = max(0, my_pos - half_w);
-                hi_r = min(hi_r, my_pos + half_w);
-            }
-        }
-        if (my_pos >= valid || my_row >= q_len) hi_r = -1;
-        st.lo_r = lo_r;
-        st.hi_r = hi_r;
-
-        const int r1 = min(r0 + 31, q_len - 1);
-        const int bp_lo = a.pos_offset + r0, bp_hi = a.pos_offset + r1;
-        int inter_lo = 0, inter_hi = valid - 1;
-        if (a.causal) inter_hi = min(inter_hi, bp_lo);
-        if (a.window > 0) {
-            if (a.causal) {
-                inter_lo = max(0, bp_hi - a.window + 1);
-            } else {
-                inter_lo = max(0, bp_hi - half_w);
-                inter_hi = min(inter_hi, bp_lo + half_w);
-            }
-        }
-        st.inter_lo = inter_lo;
-        st.inter_hi = inter_hi;
-        int union_lo = 0, union_hi = valid - 1;
-        if (a.causal) union_hi = min(union_hi, bp_hi);
-        if (a.window > 0) {
-            if (a.causal) {
-                union_lo = max(0, bp_lo - a.window + 1);
-            } else {
-                union_lo = max(0, bp_lo - half_w);
-                union_hi = min(union_hi, bp_hi + half_w);
-            }
-        }
-        if (r0 >= q_len || bp_lo >= valid) union_hi = -1;   // no row of the wave is a query
-        st.union_lo = union_lo;
-        st.union_hi = union_hi;
-        st.all_rows_valid = r0 < q_len && bp_hi < valid;
+        const RowBlockKeys k = row_block_keys(a, r0, 32, my_row, q_len, valid);
+        st.lo_r = k.lane.lo;
+        st.hi_r = k.lane.hi;
+        st.inter_lo = k.inter.lo;
+        st.inter_hi = k.inter.hi;
+        st.union_lo = k.uni.lo;
+        st.union_hi = k.uni.hi;
+        st.all_rows_valid = k.all_rows_valid;
     }
 
     // ---- Q^T operand: lane l holds row l%32, dims 16*kc + 8*g + [0, 8) ---------------
@@ -535,22 +396,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     st.vg = (const char*)((const uint16_t*)a.v + ir.kv_base);
     st.k_lds0 = lds_addr(k_lds[0]);
     st.v_lds0 = lds_addr(v_lds[0]);
-    st.k_off = (uint32_t)(((lane & 31) * ir.kv_rs + 8 * (lane >> 5)) * 2);
+    st.k_off = plan::wide_k_lane_off(lane, ir.kv_rs);
 #pragma unroll
-    for (int ii = 0; ii < G::NKW; ++ii) {
-        const int f = st.cw + kCopyWaves * ii, kb2 = f / G::KC, kc = f % G::KC;
-        st.k_cb[ii] = (uint32_t)((32 * kb2 * ir.kv_rs + 16 * kc) * 2);
-    }
+    for (int ii = 0; ii < G::NKW; ++ii) st.k_cb[ii] = plan::wide_k_copy_base(st.cw + kCopyWaves * ii, ir.kv_rs, G::KC);
+    st.v_off = plan::wide_v_lane_off(lane, ir.kv_rs);
 #pragma unroll
-    for (int ii = 0; ii < G::NVW; ++ii) {
-        const int j = st.cw + kCopyWaves * ii, c4 = j / G::DB, db = j % G::DB;
-        st.v_cb[ii] = (uint32_t)((16 * c4 * ir.kv_rs + 32 * db) * 2);
-    }
-    {
-        const int q = lane & 31;
-        const int r = 8 * (lane >> 5) + 4 * (q >> 4) + ((q & 7) >> 1);
-        st.v_off = (uint32_t)((r * ir.kv_rs + 16 * ((q >> 3) & 1) + 8 * (q & 1)) * 2);
-    }
+    for (int ii = 0; ii < G::NVW; ++ii) st.v_cb[ii] = plan::wide_v_copy_base(st.cw + kCopyWaves * ii, ir.kv_rs, G::DB);
     st.c2 = a.scale * kLog2e;
 #pragma unroll
     for (int i = 0; i < G::DB; ++i) st.o[i] = f32x16{};

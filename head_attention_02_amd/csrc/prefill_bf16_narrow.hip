@@ -36,75 +36,18 @@
 // rows at one 64-byte column group, so V rows are XOR-swizzled at 64-byte granularity:
 // chunk c of row r sits at chunk c ^ vswz(r), which puts the four rows in four
 // different quarters of the 256 bytes the banks cover.
-#include "mi_attn_device.hpp"
-#include "mi_attn_kernels.hpp"
+#include <type_traits>
+
+#include "prefill_common.hpp"
 
 namespace mi_attn {
 namespace {
 
-constexpr int kBN = 64;     // keys per tile
+constexpr int kBN = 64;     // keys per tile (plan::NarrowGeo::BN)
 constexpr float kRescaleSlack = 8.0f;  // log2 units the stale max may lag behind
-constexpr int kXcds = 8;               // accelerator complex dies (one L2 each) on MI355X
-
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 template <int D, int W>
-struct Geo {
-    static constexpr int CPR = D / 8;            // 16-byte chunks per row
-    static constexpr int KC = D / 16;            // MFMA k-steps of Q.K^T
-    static constexpr int DB = D / 32;            // 32-wide blocks of the output head dim
-    static constexpr int KS = CPR + 1;           // K row stride in chunks (padded)
-    static constexpr int NK = kBN * KS / 64;     // K copy instructions per tile
-    static constexpr int NKW = (NK + W - 1) / W; // ... per wave (at most)
-    static constexpr int NV = kBN * CPR / 64;    // V copy instructions per tile
-    static constexpr int NVW = NV / W;           // ... per wave
-    static constexpr int K_BYTES = kBN * KS * 16;
-    static constexpr int V_BYTES = kBN * CPR * 16;
-    static_assert(NV % W == 0, "V copies split evenly over the waves");
-};
-
-// V swizzle: XOR applied to the chunk index of row r (multiples of 4 chunks = 64 bytes).
-template <int D>
-__device__ __forceinline__ int vswz(int r) {
-    constexpr int QR = D / 32;        // 64-byte quarters per row
-    constexpr int RP = 4 / QR;        // rows per 256 bytes
-    return 4 * ((r / RP) & (QR - 1));
-}
-
-__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
-
-// Row max / sum over both halves of the wave (lanes l and l^32 hold the same query row).
-__device__ __forceinline__ float halves_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-
-// One 16-byte-per-lane copy from global memory straight into LDS: lane l reads
-// sbase + voff and its 16 bytes land at LDS address m0 + 16 * l (sbase and m0 are
-// wave-uniform).  Written as inline assembly so that the compiler does not track it as
-// an outstanding LDS write -- it would otherwise wait for every copy in flight
-// (vmcnt(0)), including the next tile's, before each LDS read -- and the kernel's own
-// vmcnt wait and barrier order the copies against the reads.
-__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t m0) {
-    asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(m0));
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
-}
-
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Marks a rarely taken, wave-uniform branch as having a side effect so that the compiler
-// keeps it a branch instead of computing its body on every tile and selecting.
-__device__ __forceinline__ void keep_branch() { asm volatile("" ::); }
+using Geo = plan::NarrowGeo<D, W>;
 
 template <int D, int RB, int W, bool POS_SCALE, bool F16>
 struct Prefill {
@@ -134,8 +77,9 @@ struct Prefill {
     f32x16 o[RB][G::DB];
     float m_run[RB], l_run[RB];
 
-    // Tile copies.  The tail case (rows past the valid length repeat the last valid row)
-    // is decided once per tile; whole tiles use the precomputed per-lane offsets.
+    // Tile copies (addresses from plan::narrow_k_chunk / narrow_v_chunk).  The tail case
+    // (rows past the valid length repeat the last valid row, clamped from the tile base) is
+    // decided once per tile; whole tiles use the precomputed per-lane offsets.
     __device__ __forceinline__ void copy_k(int kt, int par) {
         const char* base = kg + (size_t)kt * kBN * kv_rs * 2;
         const uint32_t lds = k_lds0 + par * G::K_BYTES + wave * 1024;
@@ -150,11 +94,9 @@ struct Prefill {
             for (int ii = 0; ii < G::NKW; ++ii) {
                 const int i = wave + W * ii;
                 if (i < G::NK) {
-                    const int p = i * 64 + lane;
-                    int row = p / G::KS, c = p - (p / G::KS) * G::KS;
-                    c = c < G::CPR ? c : 0;
-                    row = min(row, kvalid - 1 - kt * kBN);
-                    lds_dma16(base, (uint32_t)((row * kv_rs + c * 8) * 2), lds + W * ii * 1024);
+                    plan::Chunk c = plan::narrow_k_chunk(i, lane, G::CPR);
+                    c.row = plan::tail_row(c.row, kvalid, kt * kBN);
+                    lds_dma16(base, plan::chunk_offset(c, kv_rs), lds + W * ii * 1024);
                 }
             }
         }
@@ -172,11 +114,9 @@ struct Prefill {
             keep_branch();
 #pragma unroll
             for (int ii = 0; ii < G::NVW; ++ii) {
-                const int p = (wave + W * ii) * 64 + lane;
-                int row = p / G::CPR;
-                const int c = (p % G::CPR) ^ vswz<D>(row);
-                row = min(row, kvalid - 1 - kt * kBN);
-                lds_dma16(base, (uint32_t)((row * kv_rs + c * 8) * 2), lds + W * ii * 1024);
+                plan::Chunk c = plan::narrow_v_chunk(wave + W * ii, lane, D);
+                c.row = plan::tail_row(c.row, kvalid, kt * kBN);
+                lds_dma16(base, plan::chunk_offset(c, kv_rs), lds + W * ii * 1024);
             }
         }
     }
@@ -433,34 +373,14 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
     st.lane = lane;
     st.wave = wave;
     st.g = g;
-    // One-dimensional grid, q-tile slowest: for causal attention the tiles near the end of
-    // the sequence carry the most keys, so the whole grid runs longest-first and the short
-    // tiles fill in at the end instead of leaving a tail of long ones.
-    // Workgroups are dealt round-robin to the 8 XCDs (block i to XCD i % 8), each with its
-    // own L2.  When the (item, kv head) units divide evenly, every XCD gets whole units --
-    // all query heads of a kv head -- so that a unit's K/V tiles are fetched into one L2
-    // and reused there by all its query heads.
+    // block -> (q-tile, item, head): longest causal tiles first, XCD-aware (plan::map_block)
+    const plan::BlockCoord bc = plan::map_block(blockIdx.x, a.n_qtiles, a.batch, a.q_heads, a.kv_heads,
+                                                a.causal != 0, kXcds);
+    const int qt = bc.qt, b = bc.b, h = bc.h;
     const int grp = a.q_heads / a.kv_heads;
-    const int units = a.batch * a.kv_heads;
-    int qt_rank, b, h;
-    if (units % kXcds == 0) {
-        const int xcd = (int)(blockIdx.x % kXcds), k = (int)(blockIdx.x / kXcds);
-        const int per_xcd = units / kXcds;
-        const int hig = k % grp;
-        const int unit = ((k / grp) % per_xcd) * kXcds + xcd;
-        qt_rank = k / (grp * per_xcd);
-        b = unit / a.kv_heads;
-        h = (unit % a.kv_heads) * grp + hig;
-    } else {
-        const int bh = (int)(blockIdx.x % (unsigned)(a.batch * a.q_heads));
-        qt_rank = (int)(blockIdx.x / (unsigned)(a.batch * a.q_heads));
-        b = bh / a.q_heads;
-        h = bh % a.q_heads;
-    }
-    const int qt = a.causal ? (a.n_qtiles - 1 - qt_rank) : qt_rank;
     const int kvh = h / grp;
 
-    const ItemRows ir = item_rows(a, b, h, kvh, D);
+    const plan::Rows ir = item_rows(a, b, h, kvh, D);
     const int valid = ir.kv_valid;
     const int q_len = ir.q_len;
     st.kvalid = valid;
@@ -469,25 +389,12 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
     const int q0 = qt * BM;
     if (q0 >= q_len) return;   // no query row of this item in the tile (unpadded layout)
     const int last_row = min(q0 + BM, q_len) - 1;
-    const int half_w = a.window / 2;
 
-    // ---- key range of the whole workgroup -------------------------------------------
-    const int p_lo = a.pos_offset + q0;
-    const int p_hi = a.pos_offset + last_row;
-    int k_begin = 0;
-    int k_end = valid;
-    if (a.causal) k_end = min(k_end, p_hi + 1);
-    if (a.window > 0) {
-        if (a.causal) {
-            k_begin = max(k_begin, p_lo - a.window + 1);
-        } else {
-            k_begin = max(k_begin, p_lo - half_w);
-            k_end = min(k_end, p_hi + half_w + 1);
-        }
-    }
-    if (p_lo >= valid) k_end = k_begin;       // every row of the tile is padding
-    const int kt_begin = k_begin / kBN;
-    const int kt_end = k_end > k_begin ? (k_end + kBN - 1) / kBN : kt_begin;
+    // ---- key tiles of the whole workgroup: the union of its rows' key sets -------------
+    const plan::Tiles tiles = plan::key_tiles(
+        plan::span_union(a.pos_offset + q0, a.pos_offset + last_row, valid, a.causal != 0, a.window), kBN);
+    const int kt_begin = tiles.begin;
+    const int kt_end = tiles.end;
 
     // ---- per row block: this lane's query row and key interval, the block's common keys
     int my_row[RB];
@@ -495,54 +402,18 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
     for (int rb = 0; rb < RB; ++rb) {
         const int r0 = q0 + (wave * RB + rb) * 32;
         my_row[rb] = r0 + (lane & 31);
-        const int my_pos = a.pos_offset + my_row[rb];
-        int lo_r = 0, hi_r = valid - 1;
-        if (a.causal) hi_r = min(hi_r, my_pos);
-        if (a.window > 0) {
-            if (a.causal) {
-                lo_r = max(0, my_pos - a.window + 1);
-            } else {
-                lo_r = max(0, my_pos - half_w);
-                hi_r = min(hi_r, my_pos + half_w);
-            }
-        }
-        if (my_pos >= valid || my_row[rb] >= q_len) hi_r = -1;
-        st.lo_r[rb] = lo_r;
-        st.hi_r[rb] = hi_r;
-
-        const int r1 = min(r0 + 31, q_len - 1);
-        const int bp_lo = a.pos_offset + r0, bp_hi = a.pos_offset + r1;
-        int inter_lo = 0, inter_hi = valid - 1;
-        if (a.causal) inter_hi = min(inter_hi, bp_lo);
-        if (a.window > 0) {
-            if (a.causal) {
-                inter_lo = max(0, bp_hi - a.window + 1);
-            } else {
-                inter_lo = max(0, bp_hi - half_w);
-                inter_hi = min(inter_hi, bp_lo + half_w);
-            }
-        }
-        st.b_inter_lo[rb] = inter_lo;
-        st.b_inter_hi[rb] = inter_hi;
-        st.blk_all_rows_valid[rb] = r0 < q_len && bp_hi < valid;
+        const RowBlockKeys k = row_block_keys(a, r0, 32, my_row[rb], q_len, valid);
+        st.lo_r[rb] = k.lane.lo;
+        st.hi_r[rb] = k.lane.hi;
+        st.b_inter_lo[rb] = k.inter.lo;
+        st.b_inter_hi[rb] = k.inter.hi;
+        st.blk_all_rows_valid[rb] = k.all_rows_valid;
     }
     {   // the union of the key intervals of the wave's rows (all its row blocks)
         const int r0 = q0 + wave * RB * 32;
-        const int r1 = min(r0 + RB * 32 - 1, q_len - 1);
-        const int bp_lo = a.pos_offset + r0, bp_hi = a.pos_offset + r1;
-        int union_lo = 0, union_hi = valid - 1;
-        if (a.causal) union_hi = min(union_hi, bp_hi);
-        if (a.window > 0) {
-            if (a.causal) {
-                union_lo = max(0, bp_lo - a.window + 1);
-            } else {
-                union_lo = max(0, bp_lo - half_w);
-                union_hi = min(union_hi, bp_hi + half_w);
-            }
-        }
-        if (r0 >= q_len || bp_lo >= valid) union_hi = -1;   // no row of the wave is a query
-        st.union_lo = union_lo;
-        st.union_hi = union_hi;
+        const RowBlockKeys k = row_block_keys(a, r0, RB * 32, r0, q_len, valid);
+        st.union_lo = k.uni.lo;
+        st.union_hi = k.uni.hi;
     }
 
     // ---- Q^T operands: lane l holds row l%32 of each block, dims 16*kc + 8*g + [0, 8)
@@ -566,27 +437,16 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
     st.k_lds0 = lds_addr(k_lds[0]);
     st.v_lds0 = lds_addr(v_lds[0]);
 #pragma unroll
-    for (int ii = 0; ii < G::NKW; ++ii) {
-        const int p = (wave + W * ii) * 64 + lane;
-        const int row = p / G::KS;
-        int c = p - row * G::KS;
-        c = c < G::CPR ? c : 0;
-        st.koff[ii] = (uint32_t)((row * ir.kv_rs + c * 8) * 2);
-    }
-    {
-        const int p = wave * 64 + lane;
-        const int row = p / G::CPR;
-        const int c = (p % G::CPR) ^ vswz<D>(row);
-        st.voff = (uint32_t)((row * ir.kv_rs + c * 8) * 2);
-        st.v_step = (size_t)(W * 64 / G::CPR) * ir.kv_rs * 2;
-    }
+    for (int ii = 0; ii < G::NKW; ++ii) st.koff[ii] = plan::chunk_offset(plan::narrow_k_chunk(wave + W * ii, lane, G::CPR), ir.kv_rs);
+    st.voff = plan::chunk_offset(plan::narrow_v_chunk(wave, lane, D), ir.kv_rs);
+    st.v_step = plan::narrow_v_copy_step(W, D, ir.kv_rs);
     st.k_read = ((lane & 31) * G::KS + g) * 16;
     {
         const int r = 4 * g + ((lane & 15) >> 2);
 #pragma unroll
         for (int db = 0; db < G::DB; ++db) {
             const int cb = 64 * db + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);   // column byte
-            st.v_read[db] = r * 2 * D + 16 * ((cb >> 4) ^ vswz<D>(r)) + (cb & 15);
+            st.v_read[db] = r * 2 * D + 16 * ((cb >> 4) ^ plan::narrow_vswz(r, D)) + (cb & 15);
         }
     }
     st.c2 = a.scale * kLog2e;

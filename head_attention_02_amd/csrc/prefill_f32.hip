@@ -24,40 +24,22 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
     const int qt = a.causal ? (a.n_qtiles - 1 - (int)blockIdx.x) : (int)blockIdx.x;
     const int kvh = h / (a.q_heads / a.kv_heads);
 
-    const ItemRows ir = item_rows(a, b, h, kvh, D);
+    const plan::Rows ir = item_rows(a, b, h, kvh, D);
     const int valid = ir.kv_valid;
     const int q_len = ir.q_len;
 
     const int q0 = qt * kRows;
     if (q0 >= q_len) return;   // no query row of this item in the tile (unpadded layout)
     const int last_row = min(q0 + kRows, q_len) - 1;
-    const int half_w = a.window / 2;
-    const int p_lo = a.pos_offset + q0, p_hi = a.pos_offset + last_row;
-    int k_begin = 0, k_end = valid;
-    if (a.causal) k_end = min(k_end, p_hi + 1);
-    if (a.window > 0) {
-        if (a.causal) {
-            k_begin = max(k_begin, p_lo - a.window + 1);
-        } else {
-            k_begin = max(k_begin, p_lo - half_w);
-            k_end = min(k_end, p_hi + half_w + 1);
-        }
-    }
-    if (p_lo >= valid) k_end = k_begin;
+    const bool causal = a.causal != 0;
+    // key tiles of the union of the rows' key sets
+    const plan::Tiles tiles = plan::key_tiles(
+        plan::span_union(a.pos_offset + q0, a.pos_offset + last_row, valid, causal, a.window), kKeys);
 
     const int row = q0 + lane;
-    const int pos = a.pos_offset + row;
-    int lo_r = 0, hi_r = valid - 1;
-    if (a.causal) hi_r = min(hi_r, pos);
-    if (a.window > 0) {
-        if (a.causal) {
-            lo_r = max(0, pos - a.window + 1);
-        } else {
-            lo_r = max(0, pos - half_w);
-            hi_r = min(hi_r, pos + half_w);
-        }
-    }
-    if (pos >= valid || row >= q_len) hi_r = -1;
+    plan::Keys mine = plan::row_keys(a.pos_offset + row, valid, causal, a.window);
+    if (row >= q_len) mine.hi = -1;
+    const int lo_r = mine.lo, hi_r = mine.hi;
 
     const float* qrow = (const float*)a.q + ir.q_base + (size_t)min(row, q_len - 1) * ir.q_rs;
     float q[D], o[D];
@@ -70,9 +52,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
     const float* vg = (const float*)a.v + ir.kv_base;
 
     float m_run = kNegInf, l_run = 0.0f;
-    const int t_begin = k_begin / kKeys;
-    const int t_end = k_end > k_begin ? (k_end + kKeys - 1) / kKeys : t_begin;
-    for (int t = t_begin; t < t_end; ++t) {
+    for (int t = tiles.begin; t < tiles.end; ++t) {
         const int kbase = t * kKeys;
         __syncthreads();
         for (int x = lane; x < kKeys * D / 4; x += 64) {

@@ -107,6 +107,15 @@ WORKLOADS = {
 }
 
 
+def item_lengths(w: Workload):
+    """The per-item lengths a workload draws first (the same values make_inputs returns),
+    without drawing the tensors; None when the workload has none."""
+    if w.seq_len_range is None:
+        return None
+    lo, hi = w.seq_len_range
+    return np.random.default_rng(w.seed).integers(lo, hi, endpoint=True, size=w.batch).astype(np.int32)
+
+
 def make_inputs(w: Workload) -> dict:
     """Arrays for a workload, in the draw order of the recipe above.
 
