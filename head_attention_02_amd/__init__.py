@@ -300,11 +300,18 @@ def _cache_pointers(caches, B: int, name: str, dtype, device):
 
 
 def _keep_for(stream, *tensors) -> None:
-    """The pointer arrays are freed when the call returns; torch's allocator orders their
-    reuse on the current stream, so only a call on another torch stream needs this."""
-    if stream is not None and hasattr(stream, "cuda_stream"):
-        for t in tensors:
-            t.record_stream(stream)
+    """Keeps the per-call pointer arrays alive until the call's kernels have read them.
+
+    They are freed when the call returns.  On torch's current stream (stream None) the
+    allocator orders their reuse after the kernels already; on any other stream -- a torch
+    stream object or a raw hipStream_t handle -- each array is recorded on that stream,
+    so the allocator does not hand its memory out before the stream's queued work ran."""
+    if stream is None:
+        return
+    torch = _torch()
+    s = stream if hasattr(stream, "cuda_stream") else torch.cuda.ExternalStream(int(stream))
+    for t in tensors:
+        t.record_stream(s)
 
 
 def _decode_common(q, k_caches, v_caches, lens, out, workspace, what: str):

@@ -98,13 +98,13 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int bat
 /*
  * attn_prefill_token_major -- attn_prefill with every tensor token-major: the layout
  * the heads come in from the QKV projection and go out in to the output projection.
- * Follows the ferrum-kernels `Backend` page, where `flash_attention` runs between a
- * token-major -> head-major conversion of its inputs (`qk_norm_rope`: input
- * [tokens, heads, head_dim], output head-major) and `transpose_head_to_token`
- * ([heads, tokens, dim] -> [tokens, heads, dim], called after flash_attention to restore
- * token-major layout for O-proj), and the ripvec-core `Driver` page's `attn_reshape`
- * ([batch, num_heads, seq, head_dim] -> [batch * seq, hidden]); here neither
- * transpose exists.
+ * On the ferrum-kernels `Backend` page, `flash_attention` sits between two layout
+ * conversions: `qk_norm_rope` (Required Methods) turns token-major [tokens, heads,
+ * head_dim] inputs head-major, and `transpose_head_to_token` (Required Methods) turns the
+ * head-major output back token-major for the output projection; the ripvec-core
+ * `Driver` page's `attn_reshape` does the latter for [batch, num_heads, seq, head_dim].
+ * This call reads and writes the token-major tensors in place, so neither conversion
+ * exists.
  *
  *   q, out  [batch, q_len,  q_heads,  head_dim]
  *   k, v    [batch, kv_len, kv_heads, head_dim]
@@ -158,8 +158,9 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v, void* out, 
  *   window   0: all causal keys; w > 0: only the last w positions p - w < j <= p.
  *   workspace, workspace_bytes  DEVICE scratch of at least
  *            attn_decode_workspace_bytes(batch, q_heads, kv_heads, kv_len, head_dim)
- *            bytes, 256-byte aligned, not used by anything else until the call's
- *            kernels finish (the call holds partial softmax states in it).
+ *            bytes, 16-byte aligned (else MI_ATTN_ERR_INVALID), not used by anything else
+ *            until the call's kernels finish (the call holds partial softmax states in it).
+ *            May be NULL when that size is 0.
  *   batch == 0 is a valid empty call.
  */
 int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* out, int batch,
@@ -222,13 +223,21 @@ int attn_decode_append(const void* q, const void* k_new, const void* v_new, void
                        int head_dim, const int32_t* cache_lens, int window, float scale, int dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* Scratch bytes attn_decode needs for these sizes (0 when it needs none).  Pure host
- * function; returns 0 for sizes attn_decode would reject.  For attn_decode_per_cache and
- * attn_decode_append pass capacity as kv_len. */
+/* Scratch bytes attn_decode needs for these sizes (0 when it needs none): the split
+ * decode's partial states [batch, q_heads, splits, head_dim + 2] fp32 when the launch plan
+ * cuts each key range into splits.  The caller allocates them, as the pages' backends
+ * leave allocation to the caller (ripvec-core `Driver` page: drivers handle memory
+ * allocation; ferrum-kernels `Backend` page, `flash_attention_batched_per_cache`: the
+ * caller owns the buffers).  kv_heads is an argument because the plan splits per
+ * (item, kv head).  Pure host function; returns 0 for sizes attn_decode would reject.
+ * For attn_decode_per_cache and attn_decode_append pass capacity as kv_len. */
 size_t attn_decode_workspace_bytes(int batch, int q_heads, int kv_heads, int kv_len, int head_dim);
 
-/* Message of the calling thread's last failed call ("" if none).  The pointer stays
- * valid until that thread's next call into the library. */
+/* Message of the calling thread's last failed call ("" if none), "<call>: <reason>":
+ * the operation and why it was refused, after realizar `cached/attention.rs`, whose
+ * GPU paths fail with `UnsupportedOperation { operation, reason }`, and the `Result`
+ * errors of the ripvec-core `Driver` and ferrum-kernels `Backend` methods.  The pointer
+ * stays valid until that thread's next call into the library. */
 const char* attn_last_error(void);
 
 /* MI_ATTN_VERSION of the built library. */

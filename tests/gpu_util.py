@@ -1,5 +1,13 @@
 """Helpers for the GPU tests: moving the seeded numpy inputs to the device and
-comparing device results with the oracle under the stated tolerances."""
+comparing device results with the oracle under the stated tolerances.
+
+Every check returns its error summary: max-abs and max-rel error and `tol_used`, the
+largest fraction of the elementwise tolerance any element uses (1.0 = at the bound).
+`record()` prints a summary and, when MI_ATTN_PARITY_LOG names a file, appends it there as
+one JSON line, so that the margins of a run can be kept."""
+import json
+import os
+
 import numpy as np
 
 F32_MAX_ABS = 1e-4             # fp32 inputs: max-abs error against the fp64 oracle
@@ -29,12 +37,27 @@ def check(got: np.ndarray, ref: np.ndarray, dtype: str, what: str) -> dict:
     max_abs = float(err.max()) if err.size else 0.0
     max_rel = float((err / np.maximum(np.abs(ref), 1e-30)).max()) if err.size else 0.0
     if dtype == "f32":
+        tol_used = max_abs / F32_MAX_ABS
         assert max_abs <= F32_MAX_ABS, f"{what}: max abs error {max_abs:.3e} > {F32_MAX_ABS}"
     else:
         bound = BF16_ATOL + BF16_RTOL * np.abs(ref)
+        ratio = err / bound
+        tol_used = float(ratio.max()) if err.size else 0.0
         bad = err > bound
         if bad.any():
             idx = np.unravel_index(np.argmax(err - bound), err.shape)
             raise AssertionError(f"{what}: {int(bad.sum())} elements out of tolerance; worst at {idx}: "
                                  f"gpu {got[idx]:.6f} ref {ref[idx]:.6f} (max abs {max_abs:.3e})")
-    return {"max_abs": max_abs, "max_rel": max_rel}
+    return {"max_abs": max_abs, "max_rel": max_rel, "tol_used": tol_used, "elements": int(err.size)}
+
+
+def record(what: str, summary: dict) -> dict:
+    """Print a check's error summary and append it to $MI_ATTN_PARITY_LOG (JSON lines)."""
+    line = {"what": what, **summary}
+    print(f"[parity] {what}: max_abs {summary['max_abs']:.3e} max_rel {summary['max_rel']:.3e} "
+          f"tol_used {summary['tol_used']:.3f} over {summary['elements']} elements", flush=True)
+    path = os.environ.get("MI_ATTN_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(line) + "\n")
+    return summary

@@ -238,3 +238,39 @@ def test_binding_sources_hold_no_attention_arithmetic():
     src = Path(mi.__file__).read_text()
     for word in ("softmax", "exp(", "matmul", "@", "einsum", "import oracle", "scaled_dot_product"):
         assert word not in src, word
+
+
+def test_pointer_arrays_are_kept_for_every_stream_kind(monkeypatch):
+    """The per-cache calls' device pointer arrays are freed when the call returns; on a
+    stream other than torch's current one they must be recorded on that stream -- also
+    when the stream comes as a raw hipStream_t integer (wrapped as an external stream)."""
+    import torch
+
+    import head_attention_02_amd as mi
+
+    class Arr:
+        def __init__(self):
+            self.recorded = []
+
+        def record_stream(self, s):
+            self.recorded.append(s)
+
+    class TorchStream:
+        cuda_stream = 1234
+
+    made = []
+
+    def external(handle):
+        made.append(handle)
+        return ("external", handle)
+
+    monkeypatch.setattr(torch.cuda, "ExternalStream", external)
+    a, b = Arr(), Arr()
+    mi._keep_for(None, a, b)              # torch's current stream: ordered by the allocator
+    assert a.recorded == [] and b.recorded == []
+    ts = TorchStream()
+    mi._keep_for(ts, a, b)                # a torch stream object
+    assert a.recorded == [ts] and b.recorded == [ts]
+    mi._keep_for(0xBEEF, a, b)            # a raw integer handle
+    assert made == [0xBEEF]
+    assert a.recorded[-1] == ("external", 0xBEEF) and b.recorded[-1] == ("external", 0xBEEF)

@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_util import check, to_f64, to_gpu
+from gpu_util import check, record, to_f64, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -197,6 +197,6 @@ def test_named_decode_append_workload(mi, ref):
     torch.cuda.synchronize()
     want, k_after, v_after = ref.decode_append(x["q"], x["k_new"], x["v_new"], list(x["k"]), list(x["v"]),
                                                x["cache_lens"], scale=w.attn_scale, window=w.window)
-    check(to_f64(got), want, w.dtype, w.name)
+    record(w.name, check(to_f64(got), want, w.dtype, w.name))
     assert np.array_equal(_host(kd, w.dtype), np.stack(k_after)), "K caches after the append"
     assert np.array_equal(_host(vd, w.dtype), np.stack(v_after)), "V caches after the append"

@@ -1,8 +1,9 @@
 """GPU parity: libmi_attn (through its C ABI) against the fp64 oracle, element by element.
 
 Sizes span several tiles with ragged tails; the five named workloads run at full size
-in the launch configuration the benchmark times (rows sampled where the oracle would
-take too long).  bf16: |gpu - ref| <= 2e-2 + 1e-2 |ref| elementwise; fp32: max abs 1e-4.
+in the launch configuration the benchmark times, and every output element of them is
+compared with the oracle.  bf16: |gpu - ref| <= 2e-2 + 1e-2 |ref| elementwise; fp32:
+max abs 1e-4.  The named workloads' error margins are recorded (gpu_util.record).
 """
 import math
 import sys
@@ -12,7 +13,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_util import check, to_f64, to_gpu
+from gpu_util import check, record, to_f64, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -278,18 +279,11 @@ def test_repeat_runs_are_bitwise_identical(mi):
 # the five named workloads at full size
 
 
-def _sample_rows(rng, B, H, L, n_random, edges):
-    rows = {(int(b), int(h), int(i)) for b, h, i in zip(rng.integers(0, B, n_random), rng.integers(0, H, n_random),
-                                                        rng.integers(0, L, n_random))}
-    for b, h in ((0, 0), (B - 1, H - 1)):
-        for i in list(range(min(edges, L))) + list(range(max(0, L - edges), L)):
-            rows.add((b, h, i))
-    return np.array(sorted(rows), np.int32)
-
-
 @pytest.mark.parametrize("name", ["tiny_causal_f32", "bert_base_padded", "banded_w128_s8192", "causal_gqa_s4096",
                                   "causal_gqa_s4096_f16"])
 def test_named_prefill_workload(mi, ref, name):
+    """Every output row of the named workload against the oracle (the oracle runs on all
+    host cores: the causal GQA workload is 137 GFLOP of fp64 work)."""
     import torch
     w = W.WORKLOADS[name]
     say(f"workload {name}")
@@ -300,14 +294,13 @@ def test_named_prefill_workload(mi, ref, name):
                           scale=w.attn_scale)
     torch.cuda.synchronize()
     g = to_f64(got)
-    kw = dict(scale=w.attn_scale, causal=w.causal, pos_offset=w.pos_offset, seq_lens=seq, window=w.window)
-    if name in ("tiny_causal_f32", "bert_base_padded"):
-        want = ref.prefill(x["q"], x["k"], x["v"], **kw)
-        check(g, want, w.dtype, name)
-    else:
-        rows = _sample_rows(np.random.default_rng(0), w.batch, w.q_heads, w.q_len, 2000, 140)
-        want = ref.prefill(x["q"], x["k"], x["v"], rows=rows, **kw)
-        check(g[rows[:, 0], rows[:, 1], rows[:, 2]], want, w.dtype, name)
+    del got
+    want = ref.prefill(x["q"], x["k"], x["v"], scale=w.attn_scale, causal=w.causal, pos_offset=w.pos_offset,
+                       seq_lens=seq, window=w.window)
+    if seq is not None:   # padded query rows are written as zeros
+        for b in range(w.batch):
+            assert np.all(g[b, :, max(0, int(seq[b]) - w.pos_offset):] == 0.0), "padded query rows must be zero"
+    record(name, check(g, want, w.dtype, name))
 
 
 @pytest.mark.parametrize("name", ["gqa_decode_kv8192", "gqa_decode_kv8192_f16"])
@@ -321,4 +314,4 @@ def test_named_decode_workload(mi, ref, name):
     torch.cuda.synchronize()
     want = ref.decode(x["q"], x["k"], x["v"], kv_len=w.kv_len, scale=w.attn_scale, pos_offset=w.pos_offset,
                       window=w.window)
-    check(to_f64(got), want, w.dtype, name)
+    record(name, check(to_f64(got), want, w.dtype, name))
