@@ -18,6 +18,8 @@ missing library or GPU raises.
                           scale=None, workspace=None)
     attn_decode_append(q, k_new, v_new, k_caches, v_caches, cache_lens, out=None, *,
                        window=0, scale=None, workspace=None)
+    attn_decode_noalloc(q, k_cache, v_cache, out=None, *, kv_len=None, pos_offset=None,
+                        kv_lens=None, window=0, scale=None)
     attn_decode_workspace_bytes(batch, q_heads, kv_heads, kv_len, head_dim)
     attn_last_error(), attn_version()
 
@@ -39,8 +41,9 @@ LIBRARY = Path(__file__).resolve().parent / "libmi_attn.so"
 MI_ATTN_F32, MI_ATTN_BF16, MI_ATTN_F16 = 0, 1, 2
 MI_ATTN_OK, MI_ATTN_ERR_INVALID, MI_ATTN_ERR_UNSUPPORTED, MI_ATTN_ERR_HIP = 0, 1, 2, 3
 
-EXPORTS = ("attn_prefill", "attn_prefill_token_major", "attn_prefill_varlen", "attn_decode", "attn_decode_per_cache", "attn_decode_append",
-           "attn_decode_workspace_bytes", "attn_last_error", "attn_version")
+EXPORTS = ("attn_prefill", "attn_prefill_token_major", "attn_prefill_varlen", "attn_decode", "attn_decode_noalloc",
+           "attn_decode_per_cache", "attn_decode_append", "attn_decode_workspace_bytes", "attn_last_error",
+           "attn_version")
 
 
 class MiAttnError(RuntimeError):
@@ -68,6 +71,8 @@ def library() -> ctypes.CDLL:
         lib.attn_prefill_varlen.restype = i
         lib.attn_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, i, f, i, vp, sz, vp]
         lib.attn_decode.restype = i
+        lib.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, i, f, i, vp]
+        lib.attn_decode_noalloc.restype = i
         lib.attn_decode_per_cache.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, i, f, i, vp, sz, vp]
         lib.attn_decode_per_cache.restype = i
         lib.attn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, i, f, i, vp, sz, vp]
@@ -211,9 +216,7 @@ def attn_prefill_varlen(q, k, v, cu_seqlens, max_seqlen: int | None = None, out=
     return out
 
 
-def attn_decode(q, k_cache, v_cache, out=None, *, kv_len: int | None = None, pos_offset: int | None = None,
-                kv_lens=None, window: int = 0, scale: float | None = None, workspace=None, stream=None):
-    """Decode attention of one token per (item, head); returns `out` [batch, q_heads, head_dim]."""
+def _decode_args(q, k_cache, v_cache, out, kv_len, pos_offset, kv_lens):
     torch = _torch()
     if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
         raise ValueError("q must be [B,Hq,D] and the caches [B,Hkv,capacity,D]")
@@ -234,6 +237,15 @@ def attn_decode(q, k_cache, v_cache, out=None, *, kv_len: int | None = None, pos
         raise ValueError("out must match q in shape and dtype")
     if kv_lens is not None and (kv_lens.dtype != torch.int32 or kv_lens.numel() != B):
         raise ValueError("kv_lens must be an int32 tensor of batch elements")
+    return B, Hq, Hkv, cap, D, dt, kv_len, pos_offset, out
+
+
+def attn_decode(q, k_cache, v_cache, out=None, *, kv_len: int | None = None, pos_offset: int | None = None,
+                kv_lens=None, window: int = 0, scale: float | None = None, workspace=None, stream=None):
+    """Decode attention of one token per (item, head); returns `out` [batch, q_heads, head_dim]."""
+    torch = _torch()
+    B, Hq, Hkv, cap, D, dt, kv_len, pos_offset, out = _decode_args(q, k_cache, v_cache, out, kv_len, pos_offset,
+                                                                   kv_lens)
     need = attn_decode_workspace_bytes(B, Hq, Hkv, kv_len, D) if Hq % Hkv == 0 else 0
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -243,6 +255,22 @@ def attn_decode(q, k_cache, v_cache, out=None, *, kv_len: int | None = None, pos
     st = library().attn_decode(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(out, "out"),
                                B, Hq, Hkv, kv_len, cap, D, pos_offset, _dev(kv_lens, "kv_lens"), window,
                                float(scale), dt, _dev(workspace, "workspace"), ws_bytes, _stream(stream))
+    _check(st)
+    return out
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, out=None, *, kv_len: int | None = None, pos_offset: int | None = None,
+                        kv_lens=None, window: int = 0, scale: float | None = None, stream=None):
+    """attn_decode with the split partial states in the library's per-GPU scratch: the
+    library allocates nothing.  Pass `out` as well to keep the whole call free of
+    allocations (else it is allocated here, by torch, as for the other calls)."""
+    B, Hq, Hkv, cap, D, dt, kv_len, pos_offset, out = _decode_args(q, k_cache, v_cache, out, kv_len, pos_offset,
+                                                                   kv_lens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = library().attn_decode_noalloc(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                       _dev(out, "out"), B, Hq, Hkv, kv_len, cap, D, pos_offset,
+                                       _dev(kv_lens, "kv_lens"), window, float(scale), dt, _stream(stream))
     _check(st)
     return out
 

@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "mi_attn.h"
 #include "mi_attn_kernels.hpp"
@@ -81,6 +82,43 @@ int prefill_padded(const char* fn, int token_major, const void* q, const void* k
     hipError_t e = dtype != MI_ATTN_F32 ? mi_attn::launch_prefill_bf16(a, head_dim, s)
                                         : mi_attn::launch_prefill_f32(a, head_dim, s);
     if (e != hipSuccess) return fail(MI_ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return MI_ATTN_OK;
+}
+
+
+// ---- the no-allocation decode's scratch ----------------------------------------------------
+//
+// Device memory for the split decode's partial states, in the library's code object: each
+// GPU the library runs on holds its own copy from the code object's load until the process
+// ends, so attn_decode_noalloc allocates nothing.  In host code `scratch` names only a
+// host-side stand-in; its device address on the current GPU comes from
+// hipGetSymbolAddress, once per device, and only that address reaches the kernels.  The
+// split kernel writes every partial state it covers before the combine pass reads it, so
+// nothing in the scratch has to start at zero.
+constexpr size_t kScratchBytes = MI_ATTN_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+int scratch_for_current_device(const char* fn, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MI_ATTN_ERR_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: device %d is past the %d devices the library tracks", fn, dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(MI_ATTN_ERR_HIP, "%s: hipGetSymbolAddress of the scratch array failed: %s", fn,
+                        hipGetErrorString(e));
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
     return MI_ATTN_OK;
 }
 
@@ -168,12 +206,17 @@ size_t attn_decode_workspace_bytes(int batch, int q_heads, int kv_heads, int kv_
     return (size_t)batch * q_heads * p.splits * (head_dim + 2) * sizeof(float);
 }
 
-int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* out, int batch,
-                int q_heads, int kv_heads, int kv_len, int capacity, int head_dim, int pos_offset,
-                const int32_t* kv_lens, int window, float scale, int dtype, void* workspace,
-                size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// attn_decode and attn_decode_noalloc.  noalloc: the workspace is the library's scratch
+// array on the current device instead of the caller's.
+int decode_stacked(const char* fn, const void* q, const void* k_cache, const void* v_cache, void* out, int batch,
+                   int q_heads, int kv_heads, int kv_len, int capacity, int head_dim, int pos_offset,
+                   const int32_t* kv_lens, int window, float scale, int dtype, void* workspace,
+                   size_t workspace_bytes, bool noalloc, void* stream) {
     g_error[0] = '\0';
-    const char* fn = "attn_decode";
     if (dtype != MI_ATTN_BF16 && dtype != MI_ATTN_F32 && dtype != MI_ATTN_F16)
         return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
     if (batch < 0) return fail(MI_ATTN_ERR_INVALID, "%s: negative batch (%d)", fn, batch);
@@ -201,6 +244,16 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o
     if ((long)batch > 65535 || (long)q_heads > 65535)
         return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: q_heads and batch must be <= 65535", fn);
     const size_t need = attn_decode_workspace_bytes(batch, q_heads, kv_heads, kv_len, head_dim);
+    if (noalloc) {
+        if (need > kScratchBytes)
+            return fail(MI_ATTN_ERR_UNSUPPORTED,
+                        "%s: these sizes need %zu bytes of split-decode scratch, more than the %zu bytes the "
+                        "library's no-allocation scratch holds (use attn_decode with a workspace)",
+                        fn, need, kScratchBytes);
+        const int st = scratch_for_current_device(fn, &workspace);
+        if (st != MI_ATTN_OK) return st;
+        workspace_bytes = kScratchBytes;
+    }
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(MI_ATTN_ERR_INVALID, "%s: workspace of %zu bytes given, %zu needed", fn, workspace_bytes,
                     need);
@@ -229,6 +282,27 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o
                                           (hipStream_t)stream);
     if (e != hipSuccess) return fail(MI_ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return MI_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* out, int batch,
+                int q_heads, int kv_heads, int kv_len, int capacity, int head_dim, int pos_offset,
+                const int32_t* kv_lens, int window, float scale, int dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    return decode_stacked("attn_decode", q, k_cache, v_cache, out, batch, q_heads, kv_heads, kv_len, capacity,
+                          head_dim, pos_offset, kv_lens, window, scale, dtype, workspace, workspace_bytes, false,
+                          stream);
+}
+
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* out, int batch,
+                        int q_heads, int kv_heads, int kv_len, int capacity, int head_dim, int pos_offset,
+                        const int32_t* kv_lens, int window, float scale, int dtype, void* stream) {
+    return decode_stacked("attn_decode_noalloc", q, k_cache, v_cache, out, batch, q_heads, kv_heads, kv_len,
+                          capacity, head_dim, pos_offset, kv_lens, window, scale, dtype, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

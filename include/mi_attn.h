@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_VERSION 5
+#define MI_ATTN_VERSION 6
 
 typedef enum { MI_ATTN_F32 = 0, MI_ATTN_BF16 = 1, MI_ATTN_F16 = 2 } mi_attn_dtype;
 
@@ -167,6 +167,29 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o
                 int q_heads, int kv_heads, int kv_len, int capacity, int head_dim, int pos_offset,
                 const int32_t* kv_lens, int window, float scale, int dtype, void* workspace,
                 size_t workspace_bytes, void* stream);
+
+/* Bytes of the device scratch attn_decode_noalloc keeps per GPU. */
+#define MI_ATTN_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+/*
+ * attn_decode_noalloc -- attn_decode without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The call allocates nothing (no hipMalloc, no
+ * allocating library routine).  The split decode's partial states go to a scratch array
+ * of MI_ATTN_NOALLOC_SCRATCH_BYTES the library holds in device memory, one per GPU, from
+ * the library's load until the process ends; its device address is looked up once per
+ * GPU, on the first call with that GPU current (a host-side symbol query, no stream work).
+ *
+ *   Every argument and rule is attn_decode's, on the current device.  Sizes whose
+ *   partial states need more than the scratch holds (attn_decode_workspace_bytes >
+ *   MI_ATTN_NOALLOC_SCRATCH_BYTES) are refused with MI_ATTN_ERR_UNSUPPORTED.
+ *   Every call on one GPU uses that GPU's one scratch array, which keeps the last call's
+ *   partial states (nothing in it needs to start at zero).  Calls on one stream are
+ *   ordered; calls whose kernels overlap on one GPU (different streams) race on it.
+ */
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* out, int batch,
+                        int q_heads, int kv_heads, int kv_len, int capacity, int head_dim, int pos_offset,
+                        const int32_t* kv_lens, int window, float scale, int dtype, void* stream);
 
 /*
  * attn_decode_per_cache -- attn_decode over one separately allocated cache per item.

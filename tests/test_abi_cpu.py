@@ -108,6 +108,46 @@ def test_decode_empty_batch_is_ok_without_a_gpu():
     assert decode(batch=0) == mi.MI_ATTN_OK
 
 
+def decode_noalloc(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, batch=2, q_heads=8, kv_heads=2, kv_len=16, capacity=16,
+                head_dim=64, pos_offset=15, kv_lens=None, window=0, scale=0.125, dtype=mi.MI_ATTN_BF16, stream=None)
+    args.update(kw)
+    return mi.library().attn_decode_noalloc(*args.values())
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(q_heads=6, kv_heads=4), mi.MI_ATTN_ERR_INVALID, "not a multiple"),
+    (dict(kv_len=17), mi.MI_ATTN_ERR_INVALID, "capacity"),
+    (dict(pos_offset=16), mi.MI_ATTN_ERR_INVALID, "pos_offset"),
+    (dict(head_dim=48), mi.MI_ATTN_ERR_UNSUPPORTED, "head_dim 48"),
+    (dict(v=None), mi.MI_ATTN_ERR_INVALID, "null"),
+    # 511 (item, kv head) units of 8 query heads, split in two: 511 * 8 * 2 * 130 * 4 bytes of
+    # partial states, more than the scratch holds
+    (dict(batch=511, q_heads=8, kv_heads=1, head_dim=128, kv_len=4096, capacity=4096, pos_offset=4095),
+     mi.MI_ATTN_ERR_UNSUPPORTED, "scratch"),
+])
+def test_decode_noalloc_validation(kw, status, msg):
+    """The no-allocation decode validates like attn_decode, and refuses sizes whose
+    partial states exceed its fixed scratch -- all before any GPU call."""
+    assert decode_noalloc(**kw) == status
+    err = mi.attn_last_error()
+    assert err.startswith("attn_decode_noalloc: ") and msg in err
+
+
+def test_decode_noalloc_scratch_limit_matches_the_header():
+    limit = int(re.search(r"#define MI_ATTN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", HEADER.read_text())
+                .expand(r"\1")) << int(re.search(r"MI_ATTN_NOALLOC_SCRATCH_BYTES \(\d+u << (\d+)\)",
+                                                 HEADER.read_text()).group(1))
+    assert mi.attn_decode_workspace_bytes(511, 8, 1, 4096, 128) > limit
+    # the workload-sized decode needs no scratch at all, a small-batch one fits
+    assert mi.attn_decode_workspace_bytes(64, 32, 8, 8192, 128) == 0
+    assert 0 < mi.attn_decode_workspace_bytes(2, 16, 4, 3000, 128) <= limit
+
+
+def test_decode_noalloc_empty_batch_is_ok_without_a_gpu():
+    assert decode_noalloc(batch=0) == mi.MI_ATTN_OK
+
+
 def test_error_message_is_cleared_by_a_good_call():
     assert prefill(kv_heads=3) != mi.MI_ATTN_OK
     assert mi.attn_last_error()
