@@ -1,15 +1,19 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-One step = one pass over the whole path on resident synthetic inputs:
-  * prefill: causal GQA attention, batch 1, 32 query / 8 KV heads, head_dim 128,
-    q_len = kv_len = 4096, bf16 (the MFMA-bound kernel);
-  * decode: one token per (item, query head), batch 64, 32/8 heads, head_dim 128, over
-    a head-major bf16 KV cache of 8192 positions (the HBM-bound kernels).
-Prints one JSON line.  `value` is the prefill throughput in TFLOP/s of algorithmic work
-(4 * head_dim per unmasked query-key pair); the decode KV-cache bandwidth rides on the
-same line, each with a roofline object.  Kernel times come from HIP events recorded on
-the stream the kernels run on.  `--workload` benchmarks one other named workload alone.
+One step = one pass over the whole path on resident synthetic inputs: the five named
+configurations, each launched once --
+  C1 tiny_causal_f32     causal MHA, fp32, 2 heads, seq 64, head_dim 32 (latency);
+  C2 bert_base_padded    encoder, bf16, batch 32, 12 heads, head_dim 64, lengths U{16..512};
+  C3 banded_w128_s8192   banded encoder, bf16, batch 8, 12 heads, head_dim 64, |i-j| <= 64;
+  C4 causal_gqa_s4096    causal GQA prefill, bf16, 32 query / 8 KV heads, head_dim 128, 4096;
+  C5 gqa_decode_kv8192   GQA decode, bf16, batch 64, 32/8 heads, head_dim 128, 8192 keys.
+Each configuration is timed over its K launches back to back (after W warm-up launches),
+with HIP events recorded on the stream its kernels run on.  Prints one JSON line: `value`
+is C4's throughput in TFLOP/s of algorithmic work (4 * head_dim per unmasked query-key
+pair) with its roofline object, C5's KV-cache bandwidth rides beside it, and `configs`
+holds every configuration's time, rate, roofline fraction (against the larger of its MFMA
+and HBM floors) and oracle baseline.  `--workload` benchmarks one named workload alone.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
@@ -429,16 +433,73 @@ def record_mfma(run_root: Path) -> dict:
 # ---------------------------------------------------------------------------
 
 
+# The five named configurations of one step; `value` is C4's, the decode fields C5's.  The
+# memory-bound decode is timed before the matrix-core-bound causal prefill: the chip holds
+# a lower clock for a while after a long matrix-core run, which would otherwise bill the
+# prefill's power draw to the decode.
+HEADLINE = ("tiny_causal_f32", "bert_base_padded", "banded_w128_s8192", "gqa_decode_kv8192", "causal_gqa_s4096")
+HEADLINE_VALUE = "causal_gqa_s4096"
+HEADLINE_DECODE = "gqa_decode_kv8192"
+
+
+def kernel_sources(w: W.Workload):
+    if w.kind in ("decode", "decode_append"):
+        return ["decode.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]
+    if w.dtype == "f32":
+        return ["prefill_f32.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]
+    if w.head_dim == 128:
+        return ["prefill_bf16.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]
+    return ["prefill_bf16_narrow.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]
+
+
+def kernel_entry(w: W.Workload, x: dict, times_ms) -> dict:
+    """One workload's figures from its per-launch times: the mean launch time, the rate of
+    algorithmic work, and the roofline fraction -- the larger of the two floors (FLOPs at
+    the MFMA peak, bytes at the HBM peak) over the measured time; `bound` names the floor
+    that is larger.  A workload below a microsecond of floor is latency-bound: its
+    fraction is given, but the time is what counts."""
+    ms = float(np.mean(times_ms))
+    sec = ms / 1e3
+    src = kernel_sources(w)
+    if w.kind in ("decode", "decode_append"):
+        fl, by = decode_flops(w), decode_bytes(w)
+    else:
+        fl, by = prefill_flops(w, x["seq_lens"]), prefill_bytes(w, x["seq_lens"])
+    peak_f = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS   # fp16 dense = bf16 dense
+    t_mfma, t_hbm = fl / (peak_f * 1e12), by / (PEAK_HBM_GBPS * 1e9)
+    floor = max(t_mfma, t_hbm)
+    if floor < 1e-6:
+        bound = "latency"
+    else:
+        bound = "mfma" if t_mfma >= t_hbm else "hbm"
+    if bound == "hbm":
+        achieved, peak, unit = by / sec / 1e9, PEAK_HBM_GBPS, "GB/s"
+    else:
+        achieved, peak, unit = fl / sec / 1e12, peak_f, "TFLOP/s"
+    e = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": floor / sec,
+         "traffic": traffic_from_profiles(w.name, kernel_sources_digest(src)),
+         "kernel_us": ms * 1e3, "kernel_us_median": float(np.median(times_ms)) * 1e3,
+         "kernel_us_min": float(np.min(times_ms)) * 1e3,
+         "TFLOPs": fl / sec / 1e12, "frac_of_mfma_peak": fl / sec / 1e12 / peak_f,
+         "GBps": by / sec / 1e9, "frac_of_hbm_peak": by / sec / 1e9 / PEAK_HBM_GBPS,
+         "algorithmic_flop": fl, "algorithmic_bytes": by,
+         "floor_us": {"mfma": t_mfma * 1e6, "hbm": t_hbm * 1e6}}
+    if w.kind not in ("decode", "decode_append"):
+        e["mfma_counters"] = mfma_from_profiles(w.name, kernel_sources_digest(src))
+    return e
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="headline",
-                    help="headline (prefill causal_gqa_s4096 + decode gqa_decode_kv8192), a name in "
+                    help="headline (the five configurations C1-C5), a name in "
                          "workloads.WORKLOADS, or copy_calibration (1 GiB device copy for the HBM counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work per baseline")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work for the C4 and C5 baselines (half that for C1-C3)")
     ap.add_argument("--record-traffic", metavar="DIR",
                     help="no GPU run: turn the rocprofv3 FETCH_SIZE / WRITE_SIZE runs under DIR into "
                          "profiles/traffic.json")
@@ -467,7 +528,7 @@ def main() -> int:
     if args.workload == "copy_calibration":
         return copy_calibration(args.steps, args.warmup)
     if args.workload == "headline":
-        names = ["causal_gqa_s4096", "gqa_decode_kv8192"]
+        names = list(HEADLINE)
     else:
         names = [args.workload]
     ws = [W.WORKLOADS[n] for n in names]
@@ -479,88 +540,67 @@ def main() -> int:
         runners.append(Runner(w, x))
     torch.cuda.synchronize()
 
-    for _ in range(args.warmup):
-        for r in runners:
-            r()
-    torch.cuda.synchronize()
-
+    # Each workload: W warm-up launches, then K timed launches back to back, an event
+    # between every two (so that a workload runs with its own data in the caches, as a
+    # layer that calls it repeatedly would).  The K launches of all workloads are the K
+    # steps of the timed region.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(runners) + 1)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(K + 1)] for _ in runners]
     begin, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for r in runners:
+        for _ in range(args.warmup):
+            r()
     torch.cuda.synchronize()
     torch.cuda._sleep(1_000_000)   # keep the queue ahead of the GPU so events time kernels, not launches
     t0 = time.perf_counter()
     begin.record()
-    for s in range(K):
-        ev[s][0].record()
-        for i, r in enumerate(runners):
+    for i, r in enumerate(runners):
+        ev[i][0].record()
+        for s in range(K):
             r()
-            ev[s][i + 1].record()
+            ev[i][s + 1].record()
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = begin.elapsed_time(end) / K
-    per_launch = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)] for i in range(len(runners))]
-    kernel_ms = [float(np.mean(t)) for t in per_launch]
-    spread = [{"kernel_ms_median": float(np.median(t)), "kernel_ms_min": float(np.min(t))} for t in per_launch]
+    per_launch = [[ev[i][s].elapsed_time(ev[i][s + 1]) for s in range(K)] for i in range(len(runners))]
 
     result = {"metric": "attention TFLOP/s (prefill, % MFMA peak); decode KV GB/s (% HBM peak)",
               "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": step_ms,
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
               "data": "synthetic (seeded N(0, sigma^2), bf16 by round-to-nearest-even)"}
-    rooflines = {}
-    for w, x, ms, sp in zip(ws, inputs, kernel_ms, spread):
-        sec = ms / 1e3
-        if w.kind in ("prefill", "prefill_token_major", "prefill_varlen"):
-            fl = prefill_flops(w, x["seq_lens"])
-            peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS   # fp16 dense = bf16 dense
-            if w.dtype == "f32":
-                src = ["prefill_f32.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]
-            elif w.head_dim == 128:
-                src = ["prefill_bf16.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]
-            else:
-                src = ["prefill_bf16_narrow.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]
-            rooflines[w.name] = {"bound": "mfma", "achieved": fl / sec / 1e12, "peak": peak, "unit": "TFLOP/s",
-                                 "frac": fl / sec / 1e12 / peak,
-                                 "traffic": traffic_from_profiles(w.name, kernel_sources_digest(src)),
-                                 "kernel_ms": ms, **sp, "algorithmic_flop": fl,
-                                 "algorithmic_bytes": prefill_bytes(w, x["seq_lens"]),
-                                 "hbm_GBps": prefill_bytes(w, x["seq_lens"]) / sec / 1e9,
-                                 "mfma_counters": mfma_from_profiles(w.name, kernel_sources_digest(src))}
-        else:
-            by = decode_bytes(w)
-            src = ["decode.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]
-            rooflines[w.name] = {"bound": "hbm", "achieved": by / sec / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                                 "frac": by / sec / 1e9 / PEAK_HBM_GBPS,
-                                 "traffic": traffic_from_profiles(w.name, kernel_sources_digest(src)),
-                                 "kernel_ms": ms, **sp, "algorithmic_bytes": by,
-                                 "algorithmic_flop": decode_flops(w)}
-    head = ws[0]
+    rooflines = {w.name: kernel_entry(w, x, t) for w, x, t in zip(ws, inputs, per_launch)}
+    head = ws[0] if args.workload != "headline" else W.WORKLOADS[HEADLINE_VALUE]
     r0 = rooflines[head.name]
     result["value"] = r0["achieved"]
     result["unit"] = r0["unit"]
     result["dtype"] = head.dtype
     result["roofline"] = {k: r0[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
-    if len(ws) > 1:
-        r1 = rooflines[ws[1].name]
+    if args.workload == "headline":
+        r1 = rooflines[HEADLINE_DECODE]
         result["decode_kv_GBps"] = r1["achieved"]
         result["roofline_decode"] = {k: r1[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
     result["config"] = {"workload": " + ".join(f"{w.kind} {w.name}" for w in ws),
+                        "value_from": head.name,
                         "detail": {w.name: {"batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
                                             "q_len": w.q_len, "kv_len": w.kv_len, "head_dim": w.head_dim,
                                             "causal": w.causal, "window": w.window, "pos_offset": w.pos_offset,
-                                            "dtype": w.dtype} for w in ws},
-                        "kernels": rooflines}
+                                            "dtype": w.dtype} for w in ws}}
+    result["configs"] = rooflines
     result["wall_s_timed_region"] = wall
 
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (cpu_baseline)")
         for w, x in zip(ws, inputs):
+            budget = args.cpu_budget if w.name in (head.name, HEADLINE_DECODE) else args.cpu_budget / 2
             if w.kind in ("prefill", "prefill_token_major", "prefill_varlen"):
-                result.setdefault("cpu_baseline", cpu_baseline_prefill(w, x, args.cpu_budget))
+                cb = cpu_baseline_prefill(w, x, budget)
             else:
-                key = "cpu_baseline" if "cpu_baseline" not in result else "cpu_baseline_decode"
-                result[key] = cpu_baseline_decode(w, x, args.cpu_budget)
+                cb = cpu_baseline_decode(w, x, budget)
+            rooflines[w.name]["cpu_baseline"] = cb
+        result["cpu_baseline"] = rooflines[head.name]["cpu_baseline"]
+        if HEADLINE_DECODE in rooflines and head.name != HEADLINE_DECODE:
+            result["cpu_baseline_decode"] = rooflines[HEADLINE_DECODE]["cpu_baseline"]
     print(json.dumps(result), flush=True)
     return 0
 

@@ -89,6 +89,24 @@ __device__ __forceinline__ void store1(void* out, size_t at, float v) {
         ((float*)out)[at] = v;
 }
 
+// Two-element dot product of packed 16-bit pairs, accumulated in fp32:
+// c + a.lo * b.lo + a.hi * b.hi (v_dot2_f32_bf16 / v_dot2_f32_f16).
+template <int FMT>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    if constexpr (FMT == kBF16) {
+        typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+    } else {
+        typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+    }
+}
+
+// Sixteen raw bytes (eight 16-bit elements) of a cache row, non-temporal.
+__device__ __forceinline__ u32x4 load8_raw(const void* base, size_t elem) {
+    return __builtin_nontemporal_load((const u32x4*)((const uint16_t*)base + elem));
+}
+
 template <int D, int GT, int FMT, int MODE>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     constexpr int LPR = plan::DecodeGeo<D>::LPR;          // lanes per key row, 8 elements per lane
@@ -121,14 +139,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     const int s0 = kr_split.s0;
     const int s1 = kr_split.s1;
 
-    // queries of the GT heads, pre-multiplied by scale * log2(e)
+    // queries of the GT heads: fp32, pre-multiplied by scale * log2(e); 16-bit formats
+    // keep them packed as given (the scale is applied to each dot product)
+    constexpr bool PACKED = FMT != kF32;
     const float c2 = a.scale * kLog2e;
     float qf[GT][8];
+    u32x4 qw[GT];
 #pragma unroll
     for (int t = 0; t < GT; ++t) {
-        load8<FMT>(a.q, ((size_t)b * a.q_heads + h0 + t) * D + c * 8, qf[t]);
+        if constexpr (PACKED) {
+            qw[t] = *(const u32x4*)((const uint16_t*)a.q + ((size_t)b * a.q_heads + h0 + t) * D + c * 8);
+        } else {
+            load8<FMT>(a.q, ((size_t)b * a.q_heads + h0 + t) * D + c * 8, qf[t]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) qf[t][i] *= c2;
+            for (int i = 0; i < 8; ++i) qf[t][i] *= c2;
+        }
     }
 
     float m[GT], l[GT], o[GT][8];
@@ -168,40 +193,70 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     auto batch = [&](int base, auto tail_c) {
         constexpr bool TAIL = decltype(tail_c)::value;
         int key[kSteps];
-        float kx[kSteps][8];
-#pragma unroll
-        for (int u = 0; u < kSteps; ++u) {
-            key[u] = base + (u * kWaves + wave) * RPW + r;
-            const int kr = plan::decode_key_row(key[u], s0, s1, TAIL);   // out-of-range rows read a valid row
-            if constexpr (MODE == kAppend && TAIL) {
-                const bool nw = kr == pos;
-                load8<FMT, true>(nw ? a.k_new : kc, nw ? new_row : head_base + (size_t)kr * D + c * 8, kx[u]);
-            } else {
-                load8<FMT, true>(kc, head_base + (size_t)kr * D + c * 8, kx[u]);
-            }
-        }
         float s[kSteps][GT];
+        // K rows -> scores (log2 units, scale applied)
+        if constexpr (PACKED) {
+            u32x4 kw[kSteps];
 #pragma unroll
-        for (int u = 0; u < kSteps; ++u) {
+            for (int u = 0; u < kSteps; ++u) {
+                key[u] = base + (u * kWaves + wave) * RPW + r;
+                const int kr = plan::decode_key_row(key[u], s0, s1, TAIL);   // out-of-range rows read a valid row
+                if constexpr (MODE == kAppend && TAIL) {
+                    const bool nw = kr == pos;
+                    kw[u] = load8_raw(nw ? a.k_new : kc, nw ? new_row : head_base + (size_t)kr * D + c * 8);
+                } else {
+                    kw[u] = load8_raw(kc, head_base + (size_t)kr * D + c * 8);
+                }
+            }
 #pragma unroll
-            for (int t = 0; t < GT; ++t) {
-                float d = 0.0f;
+            for (int u = 0; u < kSteps; ++u) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) d = fmaf(qf[t][i], kx[u][i], d);
-                d = row_sum<LPR>(d);
-                s[u][t] = !TAIL || key[u] < s1 ? d : kNegInf;
+                for (int t = 0; t < GT; ++t) {
+                    float d = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) d = dot2<FMT>(kw[u][i], qw[t][i], d);
+                    d = row_sum<LPR>(d) * c2;
+                    s[u][t] = !TAIL || key[u] < s1 ? d : kNegInf;
+                }
+            }
+        } else {
+            float kx[kSteps][8];
+#pragma unroll
+            for (int u = 0; u < kSteps; ++u) {
+                key[u] = base + (u * kWaves + wave) * RPW + r;
+                const int kr = plan::decode_key_row(key[u], s0, s1, TAIL);
+                if constexpr (MODE == kAppend && TAIL) {
+                    const bool nw = kr == pos;
+                    load8<FMT, true>(nw ? a.k_new : kc, nw ? new_row : head_base + (size_t)kr * D + c * 8, kx[u]);
+                } else {
+                    load8<FMT, true>(kc, head_base + (size_t)kr * D + c * 8, kx[u]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kSteps; ++u) {
+#pragma unroll
+                for (int t = 0; t < GT; ++t) {
+                    float d = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) d = fmaf(qf[t][i], kx[u][i], d);
+                    d = row_sum<LPR>(d);
+                    s[u][t] = !TAIL || key[u] < s1 ? d : kNegInf;
+                }
             }
         }
-        float vx[kSteps][8];
+        // V rows (loaded before the softmax so that they are in flight during it)
+        float vx[PACKED ? 1 : kSteps][8];
+        u32x4 vw[PACKED ? kSteps : 1];
 #pragma unroll
         for (int u = 0; u < kSteps; ++u) {
             const int kr = plan::decode_key_row(key[u], s0, s1, TAIL);
-            if constexpr (MODE == kAppend && TAIL) {
-                const bool nw = kr == pos;
-                load8<FMT, true>(nw ? a.v_new : vc, nw ? new_row : head_base + (size_t)kr * D + c * 8, vx[u]);
-            } else {
-                load8<FMT, true>(vc, head_base + (size_t)kr * D + c * 8, vx[u]);
-            }
+            const bool nw = MODE == kAppend && TAIL && kr == pos;
+            const void* src = nw ? a.v_new : vc;
+            const size_t at = nw ? new_row : head_base + (size_t)kr * D + c * 8;
+            if constexpr (PACKED)
+                vw[u] = load8_raw(src, at);
+            else
+                load8<FMT, true>(src, at, vx[u]);
         }
         float m_new[GT];
         bool need_any = false;
@@ -224,18 +279,54 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
                 for (int i = 0; i < 8; ++i) o[t][i] *= alpha;
             }
         }
+        if constexpr (PACKED) {
+            // rows u and u+1 of this lane go together: each dot2 takes one element of both
+            // rows (v_perm_b32 pairs them) against the two probabilities, rounded to the
+            // cache format as the P.V products of the prefill kernels take them
+            float p[kSteps][GT];
 #pragma unroll
-        for (int t = 0; t < GT; ++t) {
-            const float m_use = m[t] == kNegInf ? 0.0f : m[t];
-            float ps = 0.0f;
+            for (int t = 0; t < GT; ++t) {
+                const float m_use = m[t] == kNegInf ? 0.0f : m[t];
+                float ps = 0.0f;
 #pragma unroll
-            for (int u = 0; u < kSteps; ++u) {
-                const float p = fast_exp2(s[u][t] - m_use);
-                ps += p;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) o[t][i] = fmaf(p, vx[u][i], o[t][i]);
+                for (int u = 0; u < kSteps; ++u) {
+                    p[u][t] = fast_exp2(s[u][t] - m_use);
+                    ps += p[u][t];
+                }
+                l[t] += ps;
             }
-            l[t] += ps;
+#pragma unroll
+            for (int u = 0; u < kSteps; u += 2) {
+                uint32_t lo[4], hi[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    lo[i] = __builtin_amdgcn_perm(vw[u + 1][i], vw[u][i], 0x05040100u);   // element 2i of rows u, u+1
+                    hi[i] = __builtin_amdgcn_perm(vw[u + 1][i], vw[u][i], 0x07060302u);   // element 2i+1
+                }
+#pragma unroll
+                for (int t = 0; t < GT; ++t) {
+                    const uint32_t pp = FMT == kBF16 ? pack_bf16x2(p[u][t], p[u + 1][t]) : pack_f16x2(p[u][t], p[u + 1][t]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        o[t][2 * i] = dot2<FMT>(lo[i], pp, o[t][2 * i]);
+                        o[t][2 * i + 1] = dot2<FMT>(hi[i], pp, o[t][2 * i + 1]);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < GT; ++t) {
+                const float m_use = m[t] == kNegInf ? 0.0f : m[t];
+                float ps = 0.0f;
+#pragma unroll
+                for (int u = 0; u < kSteps; ++u) {
+                    const float p = fast_exp2(s[u][t] - m_use);
+                    ps += p;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) o[t][i] = fmaf(p, vx[u][i], o[t][i]);
+                }
+                l[t] += ps;
+            }
         }
     };
     int base = s0;

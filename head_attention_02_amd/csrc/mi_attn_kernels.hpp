@@ -42,6 +42,13 @@ __device__ __forceinline__ plan::Rows item_rows(const PrefillArgs& a, int b, int
                            a.seq_lens ? a.seq_lens[b] : 0);
 }
 
+// Whether a prefill grid runs its q-tiles last to first (plan::map_block): a causal mask
+// puts the most keys into the last tiles, and per-item lengths (padding or unpadded items)
+// leave the last tiles only to the longest items.
+__device__ __forceinline__ bool last_tiles_first(const PrefillArgs& a) {
+    return a.causal != 0 || a.seq_lens != nullptr || a.cu_seqlens != nullptr;
+}
+
 // One decode problem, as validated and planned by attn_decode.
 struct DecodeArgs {
     const void* q;

@@ -15,7 +15,7 @@
 //
 // Work decomposition: one workgroup = 8 waves = 256 query rows of one (item, head);
 // wave w owns rows [32w, 32w+32).  The grid is one-dimensional with the q-tile index
-// slowest (longest causal tiles first) and XCD-aware.  Key tiles of 64 rows of K and V
+// slowest (longest tiles first) and XCD-aware.  Key tiles of 64 rows of K and V
 // are copied from HBM straight into LDS (global_load_lds_dwordx4, 16 bytes per lane, no
 // registers, per-lane offsets computed once), double buffered.
 //
@@ -322,9 +322,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     st.wave = wave;
     st.g = g;
     st.cw = wave - 4;
-    // block -> (q-tile, item, head): longest causal tiles first, XCD-aware (plan::map_block)
+    // block -> (q-tile, item, head): longest tiles first, XCD-aware (plan::map_block)
     const plan::BlockCoord bc = plan::map_block(blockIdx.x, a.n_qtiles, a.batch, a.q_heads, a.kv_heads,
-                                                a.causal != 0, kXcds);
+                                                last_tiles_first(a), kXcds);
     const int qt = bc.qt, b = bc.b, h = bc.h;
     const int kvh = h / (a.q_heads / a.kv_heads);
 

@@ -14,7 +14,7 @@
 //
 // Work decomposition: one workgroup = 4 waves = 128 query rows of one (item, head);
 // wave w owns rows [32w, 32w+32).  The grid is one-dimensional with the q-tile index
-// slowest (longest causal tiles first) and XCD-aware.  Key tiles of 64 rows of K and V
+// slowest (longest tiles first) and XCD-aware.  Key tiles of 64 rows of K and V
 // are copied from HBM straight into LDS (global_load_lds_dwordx4, 16 bytes per lane, no
 // registers) with per-lane offsets computed once; one barrier per tile.
 //
@@ -373,9 +373,9 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
     st.lane = lane;
     st.wave = wave;
     st.g = g;
-    // block -> (q-tile, item, head): longest causal tiles first, XCD-aware (plan::map_block)
+    // block -> (q-tile, item, head): longest tiles first, XCD-aware (plan::map_block)
     const plan::BlockCoord bc = plan::map_block(blockIdx.x, a.n_qtiles, a.batch, a.q_heads, a.kv_heads,
-                                                a.causal != 0, kXcds);
+                                                last_tiles_first(a), kXcds);
     const int qt = bc.qt, b = bc.b, h = bc.h;
     const int grp = a.q_heads / a.kv_heads;
     const int kvh = h / grp;

@@ -89,16 +89,18 @@ constexpr Tiles key_tiles(Keys k, int bn) {
 
 // ---- grid: block index -> (q-tile, item, query head) ---------------------------------
 //
-// One-dimensional grid, q-tile rank slowest.  Causal launches run the q-tiles last to
-// first: the tiles near the end of the sequence carry the most keys, so the grid runs
-// longest-first and the short tiles fill in at the end.  Workgroups are dealt
+// One-dimensional grid, q-tile rank slowest.  With `last_first` the q-tiles run last to
+// first, which runs the grid longest-first so that the short tiles fill in at the end:
+// with a causal mask the tiles near the end of the sequence carry the most keys, and with
+// per-item lengths a late q-tile exists only for the longer items (whose every tile
+// carries more keys).  Workgroups are dealt
 // round-robin to the XCDs (block i to XCD i % xcds), each with its own L2; when the
 // (item, kv head) units divide evenly, every XCD gets whole units -- all query heads of a
 // kv head -- so that a unit's K/V tiles are fetched into one L2 and reused there.
 struct BlockCoord {
     int qt, b, h;
 };
-constexpr BlockCoord map_block(unsigned block, int n_qtiles, int batch, int q_heads, int kv_heads, bool causal,
+constexpr BlockCoord map_block(unsigned block, int n_qtiles, int batch, int q_heads, int kv_heads, bool last_first,
                                int xcds) {
     const int qgrp = q_heads / kv_heads;
     const int units = batch * kv_heads;
@@ -117,7 +119,7 @@ constexpr BlockCoord map_block(unsigned block, int n_qtiles, int batch, int q_he
         b = bh / q_heads;
         h = bh % q_heads;
     }
-    return {causal ? n_qtiles - 1 - qt_rank : qt_rank, b, h};
+    return {last_first ? n_qtiles - 1 - qt_rank : qt_rank, b, h};
 }
 
 // ---- where an item's rows live ---------------------------------------------------------

@@ -182,7 +182,8 @@ void prefill(const Prefill& p) {
     std::vector<char> seen((size_t)grid, 0);
     const int qgrp = p.Hq / p.Hkv;
     for (long blk = 0; blk < grid; ++blk) {
-        const BlockCoord bc = map_block((unsigned)blk, n_qtiles, p.B, p.Hq, p.Hkv, p.causal != 0, 8);
+        const BlockCoord bc = map_block((unsigned)blk, n_qtiles, p.B, p.Hq, p.Hkv,
+                                        p.causal != 0 || !p.lens.empty() || lay == kUnpadded, 8);
         ++g_checks;
         if (bc.qt < 0 || bc.qt >= n_qtiles || bc.b < 0 || bc.b >= p.B || bc.h < 0 || bc.h >= p.Hq) {
             fail("block " + std::to_string(blk) + " maps outside the grid");
