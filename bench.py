@@ -8,8 +8,8 @@ configurations, each launched once --
   C3 banded_w128_s8192   banded encoder, bf16, batch 8, 12 heads, head_dim 64, |i-j| <= 64;
   C4 causal_gqa_s4096    causal GQA prefill, bf16, 32 query / 8 KV heads, head_dim 128, 4096;
   C5 gqa_decode_kv8192   GQA decode, bf16, batch 64, 32/8 heads, head_dim 128, 8192 keys.
-Each configuration is timed over its K launches back to back (after W warm-up launches),
-with HIP events recorded on the stream its kernels run on.  Prints one JSON line: `value`
+Each configuration in turn runs W warm-up launches and then its K timed launches back to
+back, with HIP events recorded on the stream its kernels run on.  Prints one JSON line: `value`
 is C4's throughput in TFLOP/s of algorithmic work (4 * head_dim per unmasked query-key
 pair) with its roofline object, C5's KV-cache bandwidth rides beside it, and `configs`
 holds every configuration's time, rate, roofline fraction (against the larger of its MFMA
@@ -305,14 +305,16 @@ def copy_calibration(steps: int, warmup: int) -> int:
 # ---------------------------------------------------------------------------
 # HBM traffic from rocprofv3 counter runs -> profiles/traffic.json
 
-# (run label, workload, kernel-name prefixes that make up one call, kernel sources)
-TRAFFIC_RUNS = [
-    ("head", "causal_gqa_s4096", ["prefill_bf16_kernel<128"], ["prefill_bf16.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]),
-    ("head", "gqa_decode_kv8192", ["decode_split_kernel<128", "decode_combine_kernel<128"],
-     ["decode.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]),
-    ("append", "gqa_decode_append_kv8192", ["decode_split_kernel<128", "decode_combine_kernel<128"],
-     ["decode.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]),
-]
+# The workloads whose HBM traffic is recorded (one rocprofv3 --pmc run per counter each,
+# under DIR/<workload>_<COUNTER>) and the kernel-name prefixes that make up one call.
+TRAFFIC_KERNELS = {
+    "tiny_causal_f32": ["prefill_f32_kernel<32"],
+    "bert_base_padded": ["prefill_bf16_narrow_kernel<64"],
+    "banded_w128_s8192": ["prefill_bf16_narrow_kernel<64"],
+    "gqa_decode_kv8192": ["decode_split_kernel<128", "decode_combine_kernel<128"],
+    "causal_gqa_s4096": ["prefill_bf16_kernel<128"],
+    "gqa_decode_append_kv8192": ["decode_split_kernel<128", "decode_combine_kernel<128"],
+}
 
 
 def _counter_rows(run_dir: Path, counter: str):
@@ -336,7 +338,8 @@ def _per_dispatch(rows, prefix: str) -> float:
 
 
 def record_traffic(run_root: Path) -> dict:
-    """Reads <run_root>/{head,append,copy}_{FETCH_SIZE,WRITE_SIZE} (one rocprofv3 --pmc run
+    """Reads <run_root>/<workload>_{FETCH_SIZE,WRITE_SIZE} for every workload of
+    TRAFFIC_KERNELS and <run_root>/copy_{FETCH_SIZE,WRITE_SIZE} (one rocprofv3 --pmc run
     each) and writes profiles/traffic.json: HBM bytes per call of each workload, with the
     counters scaled by what they read for the 1 GiB copy."""
     cf = _per_dispatch(_counter_rows(run_root / "copy_FETCH_SIZE", "FETCH_SIZE"), "copyBuffer")
@@ -345,13 +348,13 @@ def record_traffic(run_root: Path) -> dict:
     out = {"_calibration": {"kernel": "__amd_rocclr_copyBuffer", "bytes_read": COPY_BYTES,
                             "bytes_written": COPY_BYTES, "FETCH_SIZE_KiB": cf, "WRITE_SIZE_KiB": cw,
                             "fetch_factor": ff, "write_factor": wf}}
-    for label, name, prefixes, src in TRAFFIC_RUNS:
-        fr = _counter_rows(run_root / f"{label}_FETCH_SIZE", "FETCH_SIZE")
-        wr = _counter_rows(run_root / f"{label}_WRITE_SIZE", "WRITE_SIZE")
+    for name, prefixes in TRAFFIC_KERNELS.items():
+        fr = _counter_rows(run_root / f"{name}_FETCH_SIZE", "FETCH_SIZE")
+        wr = _counter_rows(run_root / f"{name}_WRITE_SIZE", "WRITE_SIZE")
         fk = sum(_per_dispatch(fr, p) for p in prefixes)
         wk = sum(_per_dispatch(wr, p) for p in prefixes)
         rd, wt = fk * 1024 * ff, wk * 1024 * wf
-        out[name] = {"source_digest": kernel_sources_digest(src), "kernels": prefixes,
+        out[name] = {"source_digest": kernel_sources_digest(kernel_sources(W.WORKLOADS[name])), "kernels": prefixes,
                      "FETCH_SIZE_KiB": fk, "WRITE_SIZE_KiB": wk, "bytes_read": rd, "bytes_written": wt,
                      "bytes_per_launch": rd + wt}
     (PROFILES / "traffic.json").write_text(json.dumps(out, indent=1) + "\n")
@@ -361,16 +364,13 @@ def record_traffic(run_root: Path) -> dict:
 # ---------------------------------------------------------------------------
 # Matrix-core use from rocprofv3 counter runs -> profiles/mfma.json
 
-# (workload, kernel-name prefix, kernel sources); one --pmc run each, under DIR/<workload>
+# (workload, kernel-name prefix); one --pmc run each, under DIR/<workload>
 MFMA_RUNS = [
-    ("causal_gqa_s4096", "prefill_bf16_kernel<128", ["prefill_bf16.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]),
-    ("causal_gqa_s4096_f16", "prefill_bf16_kernel<128", ["prefill_bf16.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]),
-    ("banded_w128_s8192", "prefill_bf16_narrow_kernel<64",
-     ["prefill_bf16_narrow.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]),
-    ("bert_base_padded", "prefill_bf16_narrow_kernel<64",
-     ["prefill_bf16_narrow.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]),
-    ("bert_base_varlen", "prefill_bf16_narrow_kernel<64",
-     ["prefill_bf16_narrow.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]),
+    ("causal_gqa_s4096", "prefill_bf16_kernel<128"),
+    ("causal_gqa_s4096_f16", "prefill_bf16_kernel<128"),
+    ("banded_w128_s8192", "prefill_bf16_narrow_kernel<64"),
+    ("bert_base_padded", "prefill_bf16_narrow_kernel<64"),
+    ("bert_base_varlen", "prefill_bf16_narrow_kernel<64"),
 ]
 MFMA_COUNTERS = ["GRBM_GUI_ACTIVE", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU"]
 XCDS, SIMDS = 8, 256 * 4            # MI355X: 8 XCDs, 256 CUs of 4 SIMDs
@@ -409,8 +409,9 @@ def record_mfma(run_root: Path) -> dict:
     FLOPs, and the algorithmic rate against the 16-bit dense peak."""
     out = {"_counters": MFMA_COUNTERS, "_simds": SIMDS, "_xcds": XCDS,
            "_flop_per_busy_cycle": MFMA_FLOP_PER_SIMD_CYCLE, "_peak_TFLOPs": PEAK_BF16_TFLOPS}
-    for name, prefix, src in MFMA_RUNS:
+    for name, prefix in MFMA_RUNS:
         w = W.WORKLOADS[name]
+        src = kernel_sources(w)
         seq_lens = W.make_inputs(w)["seq_lens"] if w.seq_len_range is not None else None
         c = _per_dispatch_with_time(run_root / name, prefix)
         us = c["duration_us"]
@@ -434,10 +435,8 @@ def record_mfma(run_root: Path) -> dict:
 
 
 # The five named configurations of one step; `value` is C4's, the decode fields C5's.  The
-# memory-bound decode is timed before the matrix-core-bound causal prefill: the chip holds
-# a lower clock for a while after a long matrix-core run, which would otherwise bill the
-# prefill's power draw to the decode.
-HEADLINE = ("tiny_causal_f32", "bert_base_padded", "banded_w128_s8192", "gqa_decode_kv8192", "causal_gqa_s4096")
+# two headline workloads are timed first.
+HEADLINE = ("causal_gqa_s4096", "gqa_decode_kv8192", "tiny_causal_f32", "bert_base_padded", "banded_w128_s8192")
 HEADLINE_VALUE = "causal_gqa_s4096"
 HEADLINE_DECODE = "gqa_decode_kv8192"
 
@@ -540,21 +539,22 @@ def main() -> int:
         runners.append(Runner(w, x))
     torch.cuda.synchronize()
 
-    # Each workload: W warm-up launches, then K timed launches back to back, an event
-    # between every two (so that a workload runs with its own data in the caches, as a
-    # layer that calls it repeatedly would).  The K launches of all workloads are the K
-    # steps of the timed region.
+    # Each workload in turn: W warm-up launches, then K timed launches back to back with an
+    # event between every two, so that a workload is timed in the clock and cache state
+    # its own launches leave (the chip's clock follows the power of the last milliseconds
+    # of work: a causal prefill launched right after milliseconds of HBM-bound decode ran
+    # its first launches 20 % slower).  The K launches of all workloads are the K steps of
+    # the timed region.
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(K + 1)] for _ in runners]
     begin, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for r in runners:
-        for _ in range(args.warmup):
-            r()
     torch.cuda.synchronize()
-    torch.cuda._sleep(1_000_000)   # keep the queue ahead of the GPU so events time kernels, not launches
     t0 = time.perf_counter()
     begin.record()
     for i, r in enumerate(runners):
+        for _ in range(args.warmup):
+            r()
+        torch.cuda._sleep(1_000_000)   # keep the queue ahead of the GPU so events time kernels, not launches
         ev[i][0].record()
         for s in range(K):
             r()
@@ -562,8 +562,8 @@ def main() -> int:
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = begin.elapsed_time(end) / K
     per_launch = [[ev[i][s].elapsed_time(ev[i][s + 1]) for s in range(K)] for i in range(len(runners))]
+    step_ms = sum(ev[i][0].elapsed_time(ev[i][K]) for i in range(len(runners))) / K
 
     result = {"metric": "attention TFLOP/s (prefill, % MFMA peak); decode KV GB/s (% HBM peak)",
               "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": step_ms,

@@ -29,7 +29,6 @@ namespace {
 
 constexpr int kWaves = plan::DecodeGeo<128>::WAVES;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kSteps = plan::DecodeGeo<128>::STEPS;   // wave loads per batch (rows per lane group between softmax updates)
 constexpr float kRescaleSlack = 8.0f;   // log2 units the stale running max may lag behind
 
 // Eight consecutive elements as fp32.  STREAM marks a load of cache rows, which are read
@@ -107,21 +106,47 @@ __device__ __forceinline__ u32x4 load8_raw(const void* base, size_t elem) {
     return __builtin_nontemporal_load((const u32x4*)((const uint16_t*)base + elem));
 }
 
+// Merges the online-softmax states (m, l, o) of the lanes lane ^ x for x = first,
+// 2*first, ..., 32 (the row streams of one wave that hold the same elements): every lane
+// ends with the merge of its group.
+template <int GT, int EPL>
+__device__ __forceinline__ void merge_lanes(float (&m)[GT], float (&l)[GT], float (&o)[GT][EPL], int first) {
+    for (int x = first; x < 64; x *= 2) {
+#pragma unroll
+        for (int t = 0; t < GT; ++t) {
+            const float mo = __shfl_xor(m[t], x), lo = __shfl_xor(l[t], x);
+            const float mm = fmaxf(m[t], mo);
+            const float m_use = mm == kNegInf ? 0.0f : mm;
+            const float a1 = fast_exp2(m[t] - m_use), a2 = fast_exp2(mo - m_use);
+            l[t] = l[t] * a1 + lo * a2;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) o[t][i] = o[t][i] * a1 + __shfl_xor(o[t][i], x) * a2;
+            m[t] = mm;
+        }
+    }
+}
+
 template <int D, int GT, int FMT, int MODE>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
-    constexpr int LPR = plan::DecodeGeo<D>::LPR;          // lanes per key row, 8 elements per lane
-    constexpr int RPW = plan::DecodeGeo<D>::RPW;          // rows per wave load
-    constexpr int STREAMS = plan::DecodeGeo<D>::STREAMS;  // independent row streams in the workgroup
-    constexpr int BATCH = plan::DecodeGeo<D>::BATCH;
+    // 16-bit caches are read as packed pairs, EPL (8 or 16) elements per lane and row:
+    // word w (8 elements, 16 bytes) of lane c holds elements w*D/NW + 8c + [0, 8), so that
+    // each load instruction reads whole 128-byte runs of its rows
+    constexpr bool PACKED = FMT != kF32;
+    constexpr int EPL = PACKED && D >= 64 ? 16 : 8;
+    constexpr int NW = EPL / 8;                                      // 16-byte words per lane and row
+    using DG = plan::DecodeGeo<D, EPL>;
+    constexpr int LPR = DG::LPR;          // lanes per key row
+    constexpr int RPW = DG::RPW;          // rows per wave load
+    constexpr int BATCH = DG::BATCH;
+    constexpr int kSteps = DG::STEPS;     // wave loads per batch (rows per lane group between softmax updates)
 
-    __shared__ float s_m[STREAMS][GT];
-    __shared__ float s_l[STREAMS][GT];
-    __shared__ float s_o[STREAMS][GT][D];
+    __shared__ float s_m[kWaves][GT];
+    __shared__ float s_l[kWaves][GT];
+    __shared__ float s_o[kWaves][GT][D];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int r = lane / LPR, c = lane % LPR;
-    const int stream = wave * RPW + r;
     const int b = blockIdx.z;
     const int kvh = blockIdx.y / a.head_groups;
     const int hg = blockIdx.y % a.head_groups;
@@ -141,28 +166,29 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 
     // queries of the GT heads: fp32, pre-multiplied by scale * log2(e); 16-bit formats
     // keep them packed as given (the scale is applied to each dot product)
-    constexpr bool PACKED = FMT != kF32;
     const float c2 = a.scale * kLog2e;
     float qf[GT][8];
-    u32x4 qw[GT];
+    u32x4 qw[GT][NW];
 #pragma unroll
     for (int t = 0; t < GT; ++t) {
+        const size_t q_at = ((size_t)b * a.q_heads + h0 + t) * D + 8 * c;
         if constexpr (PACKED) {
-            qw[t] = *(const u32x4*)((const uint16_t*)a.q + ((size_t)b * a.q_heads + h0 + t) * D + c * 8);
+#pragma unroll
+            for (int w = 0; w < NW; ++w) qw[t][w] = *(const u32x4*)((const uint16_t*)a.q + q_at + w * (D / NW));
         } else {
-            load8<FMT>(a.q, ((size_t)b * a.q_heads + h0 + t) * D + c * 8, qf[t]);
+            load8<FMT>(a.q, q_at, qf[t]);
 #pragma unroll
             for (int i = 0; i < 8; ++i) qf[t][i] *= c2;
         }
     }
 
-    float m[GT], l[GT], o[GT][8];
+    float m[GT], l[GT], o[GT][EPL];
 #pragma unroll
     for (int t = 0; t < GT; ++t) {
         m[t] = kNegInf;
         l[t] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[t][i] = 0.0f;
+        for (int i = 0; i < EPL; ++i) o[t][i] = 0.0f;
     }
 
     const void* kc = a.k;
@@ -177,36 +203,39 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     // lanes that read it), not from the cache; the split that holds the position also
     // stores the new rows into the cache (first head group only).  No other workgroup
     // reads that slot, so the store does not race with the reads.
-    const size_t new_row = ((size_t)b * a.kv_heads + kvh) * D + c * 8;
+    const size_t new_row = ((size_t)b * a.kv_heads + kvh) * D + 8 * c;
     if constexpr (MODE == kAppend) {
         if (hg == 0 && pos >= s0 && pos < s1 && tid < LPR) {
-            copy8<FMT>(a.k_new, new_row, (void*)kc, head_base + (size_t)pos * D + c * 8);
-            copy8<FMT>(a.v_new, new_row, (void*)vc, head_base + (size_t)pos * D + c * 8);
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                copy8<FMT>(a.k_new, new_row + w * (D / NW), (void*)kc, head_base + (size_t)pos * D + 8 * c + w * (D / NW));
+                copy8<FMT>(a.v_new, new_row + w * (D / NW), (void*)vc, head_base + (size_t)pos * D + 8 * c + w * (D / NW));
+            }
         }
     }
     // One batch of kSteps wave loads per lane group.  TAIL: the last batch of the key range;
     // it may reach past the end, so its rows are clamped to a valid one and masked, and it
     // holds the query position, the only row an append takes from the new token (key
-    // s1 - 1 when this split holds the position).  The other batches skip all three.  The running max is moved lazily, only when a batch's max
-    // exceeds it by more than 2^8 (p <= 256 otherwise; o and l share the stale max, so
-    // the merge below and the combine pass are unchanged).
+    // s1 - 1 when this split holds the position).  The other batches skip all three.  The
+    // running max is moved lazily, only when a batch's max exceeds it by more than 2^8
+    // (p <= 256 otherwise; o and l share the stale max, so the merges below and the
+    // combine pass are unchanged).
     auto batch = [&](int base, auto tail_c) {
         constexpr bool TAIL = decltype(tail_c)::value;
         int key[kSteps];
         float s[kSteps][GT];
         // K rows -> scores (log2 units, scale applied)
         if constexpr (PACKED) {
-            u32x4 kw[kSteps];
+            u32x4 kw[kSteps][NW];
 #pragma unroll
             for (int u = 0; u < kSteps; ++u) {
                 key[u] = base + (u * kWaves + wave) * RPW + r;
                 const int kr = plan::decode_key_row(key[u], s0, s1, TAIL);   // out-of-range rows read a valid row
-                if constexpr (MODE == kAppend && TAIL) {
-                    const bool nw = kr == pos;
-                    kw[u] = load8_raw(nw ? a.k_new : kc, nw ? new_row : head_base + (size_t)kr * D + c * 8);
-                } else {
-                    kw[u] = load8_raw(kc, head_base + (size_t)kr * D + c * 8);
-                }
+                const bool nw = MODE == kAppend && TAIL && kr == pos;
+                const void* src = nw ? a.k_new : kc;
+                const size_t at = nw ? new_row : head_base + (size_t)kr * D + 8 * c;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) kw[u][w] = load8_raw(src, at + w * (D / NW));
             }
 #pragma unroll
             for (int u = 0; u < kSteps; ++u) {
@@ -214,7 +243,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
                 for (int t = 0; t < GT; ++t) {
                     float d = 0.0f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) d = dot2<FMT>(kw[u][i], qw[t][i], d);
+                    for (int w = 0; w < NW; ++w)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) d = dot2<FMT>(kw[u][w][i], qw[t][w][i], d);
                     d = row_sum<LPR>(d) * c2;
                     s[u][t] = !TAIL || key[u] < s1 ? d : kNegInf;
                 }
@@ -225,12 +256,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
             for (int u = 0; u < kSteps; ++u) {
                 key[u] = base + (u * kWaves + wave) * RPW + r;
                 const int kr = plan::decode_key_row(key[u], s0, s1, TAIL);
-                if constexpr (MODE == kAppend && TAIL) {
-                    const bool nw = kr == pos;
-                    load8<FMT, true>(nw ? a.k_new : kc, nw ? new_row : head_base + (size_t)kr * D + c * 8, kx[u]);
-                } else {
-                    load8<FMT, true>(kc, head_base + (size_t)kr * D + c * 8, kx[u]);
-                }
+                const bool nw = MODE == kAppend && TAIL && kr == pos;
+                load8<FMT, true>(nw ? a.k_new : kc, nw ? new_row : head_base + (size_t)kr * D + 8 * c, kx[u]);
             }
 #pragma unroll
             for (int u = 0; u < kSteps; ++u) {
@@ -246,17 +273,19 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         }
         // V rows (loaded before the softmax so that they are in flight during it)
         float vx[PACKED ? 1 : kSteps][8];
-        u32x4 vw[PACKED ? kSteps : 1];
+        u32x4 vw[PACKED ? kSteps : 1][NW];
 #pragma unroll
         for (int u = 0; u < kSteps; ++u) {
             const int kr = plan::decode_key_row(key[u], s0, s1, TAIL);
             const bool nw = MODE == kAppend && TAIL && kr == pos;
             const void* src = nw ? a.v_new : vc;
-            const size_t at = nw ? new_row : head_base + (size_t)kr * D + c * 8;
-            if constexpr (PACKED)
-                vw[u] = load8_raw(src, at);
-            else
+            const size_t at = nw ? new_row : head_base + (size_t)kr * D + 8 * c;
+            if constexpr (PACKED) {
+#pragma unroll
+                for (int w = 0; w < NW; ++w) vw[u][w] = load8_raw(src, at + w * (D / NW));
+            } else {
                 load8<FMT, true>(src, at, vx[u]);
+            }
         }
         float m_new[GT];
         bool need_any = false;
@@ -276,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
                 m[t] = need ? m_new[t] : m[t];
                 l[t] *= alpha;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) o[t][i] *= alpha;
+                for (int i = 0; i < EPL; ++i) o[t][i] *= alpha;
             }
         }
         if constexpr (PACKED) {
@@ -297,20 +326,24 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
             }
 #pragma unroll
             for (int u = 0; u < kSteps; u += 2) {
-                uint32_t lo[4], hi[4];
+                uint32_t lo[NW][4], hi[NW][4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    lo[i] = __builtin_amdgcn_perm(vw[u + 1][i], vw[u][i], 0x05040100u);   // element 2i of rows u, u+1
-                    hi[i] = __builtin_amdgcn_perm(vw[u + 1][i], vw[u][i], 0x07060302u);   // element 2i+1
-                }
+                for (int w = 0; w < NW; ++w)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        lo[w][i] = __builtin_amdgcn_perm(vw[u + 1][w][i], vw[u][w][i], 0x05040100u);   // element 2i of rows u, u+1
+                        hi[w][i] = __builtin_amdgcn_perm(vw[u + 1][w][i], vw[u][w][i], 0x07060302u);   // element 2i+1
+                    }
 #pragma unroll
                 for (int t = 0; t < GT; ++t) {
                     const uint32_t pp = FMT == kBF16 ? pack_bf16x2(p[u][t], p[u + 1][t]) : pack_f16x2(p[u][t], p[u + 1][t]);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        o[t][2 * i] = dot2<FMT>(lo[i], pp, o[t][2 * i]);
-                        o[t][2 * i + 1] = dot2<FMT>(hi[i], pp, o[t][2 * i + 1]);
-                    }
+                    for (int w = 0; w < NW; ++w)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            o[t][8 * w + 2 * i] = dot2<FMT>(lo[w][i], pp, o[t][8 * w + 2 * i]);
+                            o[t][8 * w + 2 * i + 1] = dot2<FMT>(hi[w][i], pp, o[t][8 * w + 2 * i + 1]);
+                        }
                 }
             }
         } else {
@@ -333,26 +366,30 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     for (; base + BATCH < s1; base += BATCH) batch(base, std::integral_constant<bool, false>{});
     if (base < s1) batch(base, std::integral_constant<bool, true>{});
 
-    // merge the workgroup's row streams
+    // merge the row streams: first those of each wave (lanes with the same elements), then
+    // the waves' through LDS
+    merge_lanes<GT, EPL>(m, l, o, LPR);
+    if (r == 0) {
 #pragma unroll
-    for (int t = 0; t < GT; ++t) {
-        if (c == 0) {
-            s_m[stream][t] = m[t];
-            s_l[stream][t] = l[t];
+        for (int t = 0; t < GT; ++t) {
+            if (c == 0) {
+                s_m[wave][t] = m[t];
+                s_l[wave][t] = l[t];
+            }
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) s_o[wave][t][(i / 8) * (D / NW) + 8 * c + i % 8] = o[t][i];
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s_o[stream][t][c * 8 + i] = o[t][i];
     }
     __syncthreads();
     for (int x = tid; x < GT * D; x += kThreads) {
         const int t = x / D, d = x % D;
         float mm = kNegInf;
 #pragma unroll
-        for (int st = 0; st < STREAMS; ++st) mm = fmaxf(mm, s_m[st][t]);
+        for (int st = 0; st < kWaves; ++st) mm = fmaxf(mm, s_m[st][t]);
         const float m_use = mm == kNegInf ? 0.0f : mm;
         float acc = 0.0f, ll = 0.0f;
 #pragma unroll
-        for (int st = 0; st < STREAMS; ++st) {
+        for (int st = 0; st < kWaves; ++st) {
             const float w = fast_exp2(s_m[st][t] - m_use);
             acc = fmaf(w, s_o[st][t][d], acc);
             ll = fmaf(w, s_l[st][t], ll);

@@ -281,14 +281,15 @@ constexpr size_t narrow_v_copy_step(int waves, int D, int kv_rs) { return (size_
 
 // ---- decode launch plan --------------------------------------------------------------------
 
-// Decode split kernel shape: 4 waves; each K/V row (D elements) is read by D/8 lanes with
-// one 16-byte load each, so a wave load covers 64/(D/8) rows; a batch is 8 wave loads
-// per row stream between two softmax updates.
-template <int D>
+// Decode split kernel shape: 4 waves; each K/V row (D elements) is read by D/EPL lanes
+// with EPL/8 16-byte loads each, so a wave load covers 64/(D/EPL) rows; a batch is STEPS
+// wave loads per row stream between two softmax updates.  EPL is 16 for 16-bit caches at
+// head dims 64 and 128 (fewer lanes per row: fewer cross-lane sums per byte), else 8.
+template <int D, int EPL = 8>
 struct DecodeGeo {
     static constexpr int WAVES = 4;
-    static constexpr int STEPS = 8;
-    static constexpr int LPR = D / 8;              // lanes per key row
+    static constexpr int STEPS = EPL == 16 ? 4 : 8;
+    static constexpr int LPR = D / EPL;            // lanes per key row
     static constexpr int RPW = 64 / LPR;           // rows per wave load
     static constexpr int STREAMS = RPW * WAVES;    // independent row streams in the workgroup
     static constexpr int BATCH = STREAMS * STEPS;  // keys per batch

@@ -227,9 +227,11 @@ void prefill(const Prefill& p) {
         }
 }
 
-template <int D>
+// EPL: elements per lane and row (8 for fp32 caches and head dim 32, 16 for 16-bit caches
+// at head dims 64 and 128); both shapes are checked where both can run.
+template <int D, int EPL>
 void decode(int mode, int B, int Hq, int Hkv, int cap, int kv_len, int P, int window, const std::vector<int>& lens) {
-    using G = DecodeGeo<D>;
+    using G = DecodeGeo<D, EPL>;
     const int len_arg = mode == 0 ? kv_len : cap;
     const DecodePlan pl = decode_plan(B, Hq, Hkv, len_arg, 512);
     const size_t head_extent = (size_t)cap * D;   // one (item, kv head) cache
@@ -297,11 +299,14 @@ int main(int argc, char** argv) {
                 return 2;
             }
             if (D == 32)
-                decode<32>(mode, B, Hq, Hkv, cap, kv_len, P, W, lens);
-            else if (D == 64)
-                decode<64>(mode, B, Hq, Hkv, cap, kv_len, P, W, lens);
-            else
-                decode<128>(mode, B, Hq, Hkv, cap, kv_len, P, W, lens);
+                decode<32, 8>(mode, B, Hq, Hkv, cap, kv_len, P, W, lens);
+            else if (D == 64) {
+                decode<64, 8>(mode, B, Hq, Hkv, cap, kv_len, P, W, lens);
+                decode<64, 16>(mode, B, Hq, Hkv, cap, kv_len, P, W, lens);
+            } else {
+                decode<128, 8>(mode, B, Hq, Hkv, cap, kv_len, P, W, lens);
+                decode<128, 16>(mode, B, Hq, Hkv, cap, kv_len, P, W, lens);
+            }
         }
     }
     if (g_fails) {

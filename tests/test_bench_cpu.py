@@ -70,7 +70,7 @@ def test_record_mfma(tmp_path, monkeypatch):
     run = tmp_path / "runs"
     # every workload: two dispatches of 100 us and 120 us at 2.0 GHz on each XCD, MFMA busy
     # half the cycles, plus a dispatch of another kernel that must be ignored
-    for name, prefix, _ in bench.MFMA_RUNS:
+    for name, prefix in bench.MFMA_RUNS:
         rows = []
         for d, us in ((1, 100.0), (2, 120.0)):
             cyc = 2.0e3 * us
@@ -82,7 +82,7 @@ def test_record_mfma(tmp_path, monkeypatch):
         _write_counters(run / name, rows)
     out = bench.record_mfma(run)
     saved = json.loads((tmp_path / "profiles" / "mfma.json").read_text())
-    for name, _, _ in bench.MFMA_RUNS:
+    for name, _ in bench.MFMA_RUNS:
         r = out[name]
         assert saved[name] == r
         assert r["dispatches"] == 2
@@ -106,22 +106,26 @@ def test_record_traffic(tmp_path, monkeypatch):
     # the copy reads 1 GiB and the counter shows half of it: every FETCH is scaled by 2
     _write_counters(run / "copy_FETCH_SIZE", [(1, "__amd_rocclr_copyBuffer", "FETCH_SIZE", gib_kib / 2, 0, 1)])
     _write_counters(run / "copy_WRITE_SIZE", [(1, "__amd_rocclr_copyBuffer", "WRITE_SIZE", gib_kib, 0, 1)])
-    for label in {r[0] for r in bench.TRAFFIC_RUNS}:
-        _write_counters(run / f"{label}_FETCH_SIZE",
-                        [(1, "void mi_attn::prefill_bf16_kernel<128, true, false>(a)", "FETCH_SIZE", 100.0, 0, 1),
-                         (2, "void mi_attn::decode_split_kernel<128, 4, 1, 0>(a)", "FETCH_SIZE", 1000.0, 0, 1),
-                         (3, "void mi_attn::decode_split_kernel<128, 4, 1, 0>(a)", "FETCH_SIZE", 3000.0, 0, 1)])
-        _write_counters(run / f"{label}_WRITE_SIZE",
-                        [(1, "void mi_attn::prefill_bf16_kernel<128, true, false>(a)", "WRITE_SIZE", 10.0, 0, 1),
-                         (2, "void mi_attn::decode_split_kernel<128, 4, 1, 0>(a)", "WRITE_SIZE", 4.0, 0, 1)])
+    # every workload's run holds its own kernel (two dispatches, 1000 and 3000 KiB read) and
+    # a dispatch of another kernel that must be ignored
+    for name, prefixes in bench.TRAFFIC_KERNELS.items():
+        fetch = [(1, "void mi_attn::some_other_kernel(a)", "FETCH_SIZE", 1e9, 0, 1)]
+        write = [(1, "void mi_attn::some_other_kernel(a)", "WRITE_SIZE", 1e9, 0, 1)]
+        for p in prefixes:
+            fetch += [(2, f"void mi_attn::{p}, 4, 1, 0>(a)", "FETCH_SIZE", 1000.0, 0, 1),
+                      (3, f"void mi_attn::{p}, 4, 1, 0>(a)", "FETCH_SIZE", 3000.0, 0, 1)]
+            write += [(2, f"void mi_attn::{p}, 4, 1, 0>(a)", "WRITE_SIZE", 4.0, 0, 1)]
+        _write_counters(run / f"{name}_FETCH_SIZE", fetch)
+        _write_counters(run / f"{name}_WRITE_SIZE", write)
     out = bench.record_traffic(run)
     assert out["_calibration"]["fetch_factor"] == pytest.approx(2.0)
     assert out["_calibration"]["write_factor"] == pytest.approx(1.0)
-    assert out["causal_gqa_s4096"]["bytes_read"] == pytest.approx(100.0 * 1024 * 2)
-    assert out["causal_gqa_s4096"]["bytes_written"] == pytest.approx(10.0 * 1024)
-    # the decode's two dispatches average 2000 KiB read
-    assert out["gqa_decode_kv8192"]["bytes_read"] == pytest.approx(2000.0 * 1024 * 2)
-    assert out["gqa_decode_kv8192"]["bytes_per_launch"] == pytest.approx(2000.0 * 1024 * 2 + 4.0 * 1024)
+    for name, prefixes in bench.TRAFFIC_KERNELS.items():
+        n = len(prefixes)   # the decode's call is two kernels, each counted once per call
+        assert out[name]["bytes_read"] == pytest.approx(n * 2000.0 * 1024 * 2)
+        assert out[name]["bytes_written"] == pytest.approx(n * 4.0 * 1024)
+        assert out[name]["source_digest"] == bench.kernel_sources_digest(bench.kernel_sources(W.WORKLOADS[name]))
+    assert set(bench.HEADLINE) <= set(bench.TRAFFIC_KERNELS)
 
 
 def test_more_than_one_gpu_is_refused(capsys, monkeypatch):
