@@ -1,25 +1,30 @@
 // prefill_f32.hip -- attention prefill for fp32 inputs (the accuracy path).
 //
 // Same single-pass, online-softmax algorithm as the bf16 kernel, in plain fp32 on the
-// vector ALUs: each lane owns one query row (its q and its output accumulator live in
-// registers), key/value tiles are staged in LDS and read by every lane at the same
-// address (a broadcast).  Only the keys of the row's key set contribute; tiles outside
-// the union of the rows' key ranges are never loaded.
+// vector ALUs: each query row is held by eight lanes, each with an eighth of the row's q
+// and output accumulator in registers; a score is the sum of the eight partial dot
+// products (cross-lane adds within the group of eight).  Key/value tiles are staged in
+// LDS and read by the rows' lanes at the same addresses (a broadcast).  Only the keys of
+// the row's key set contribute; tiles outside the union of the rows' key ranges are
+// never loaded.
 #include "mi_attn_device.hpp"
 #include "mi_attn_kernels.hpp"
 
 namespace mi_attn {
 namespace {
 
-constexpr int kRows = 64;   // query rows per workgroup (one wave)
+constexpr int kRows = 64;   // query rows per workgroup
+constexpr int kLpr = 8;     // lanes per query row
 constexpr int kKeys = 32;   // keys per LDS tile
 
 template <int D>
-__global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kRows * kLpr) void prefill_f32_kernel(PrefillArgs a) {
+    constexpr int DQ = D / kLpr;   // dims per lane
     __shared__ __attribute__((aligned(16))) float k_lds[kKeys * D];
     __shared__ __attribute__((aligned(16))) float v_lds[kKeys * D];
 
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int part = tid % kLpr;
     const int b = blockIdx.z, h = blockIdx.y;
     const int qt = a.causal ? (a.n_qtiles - 1 - (int)blockIdx.x) : (int)blockIdx.x;
     const int kvh = h / (a.q_heads / a.kv_heads);
@@ -36,15 +41,15 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
     const plan::Tiles tiles = plan::key_tiles(
         plan::span_union(a.pos_offset + q0, a.pos_offset + last_row, valid, causal, a.window), kKeys);
 
-    const int row = q0 + lane;
+    const int row = q0 + tid / kLpr;
     plan::Keys mine = plan::row_keys(a.pos_offset + row, valid, causal, a.window);
     if (row >= q_len) mine.hi = -1;
     const int lo_r = mine.lo, hi_r = mine.hi;
 
-    const float* qrow = (const float*)a.q + ir.q_base + (size_t)min(row, q_len - 1) * ir.q_rs;
-    float q[D], o[D];
+    const float* qrow = (const float*)a.q + ir.q_base + (size_t)min(row, q_len - 1) * ir.q_rs + part * DQ;
+    float q[DQ], o[DQ];
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
+    for (int d = 0; d < DQ; ++d) {
         q[d] = row < q_len ? qrow[d] : 0.0f;
         o[d] = 0.0f;
     }
@@ -55,7 +60,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
     for (int t = tiles.begin; t < tiles.end; ++t) {
         const int kbase = t * kKeys;
         __syncthreads();
-        for (int x = lane; x < kKeys * D / 4; x += 64) {
+        for (int x = tid; x < kKeys * D / 4; x += kRows * kLpr) {
             const int r = x / (D / 4), c4 = x % (D / 4);
             const int j = kbase + r;
             f32x4 kk = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
@@ -74,7 +79,8 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
         for (int jj = 0; jj < kKeys; ++jj) {
             float dot = 0.0f;
 #pragma unroll
-            for (int d = 0; d < D; ++d) dot = fmaf(q[d], k_lds[jj * D + d], dot);
+            for (int d = 0; d < DQ; ++d) dot = fmaf(q[d], k_lds[jj * D + part * DQ + d], dot);
+            dot = row_sum<kLpr>(dot);   // the row's eight parts
             const int j = kbase + jj;
             s[jj] = (j >= lo_r && j <= hi_r) ? dot * a.scale : kNegInf;
             mx = fmaxf(mx, s[jj]);
@@ -85,21 +91,21 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
         m_run = m_new;
         l_run *= alpha;
 #pragma unroll
-        for (int d = 0; d < D; ++d) o[d] *= alpha;
+        for (int d = 0; d < DQ; ++d) o[d] *= alpha;
 #pragma unroll
         for (int jj = 0; jj < kKeys; ++jj) {
             const float p = expf(s[jj] - m_use);
             l_run += p;
 #pragma unroll
-            for (int d = 0; d < D; ++d) o[d] = fmaf(p, v_lds[jj * D + d], o[d]);
+            for (int d = 0; d < DQ; ++d) o[d] = fmaf(p, v_lds[jj * D + part * DQ + d], o[d]);
         }
     }
 
     if (row >= q_len) return;
     const float inv = (hi_r >= 0 && l_run > 0.0f) ? 1.0f / l_run : 0.0f;
-    float* orow = (float*)a.out + ir.q_base + (size_t)row * ir.q_rs;
+    float* orow = (float*)a.out + ir.q_base + (size_t)row * ir.q_rs + part * DQ;
 #pragma unroll
-    for (int d = 0; d < D; d += 4) *(f32x4*)(orow + d) = f32x4{o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv};
+    for (int d = 0; d < DQ; d += 4) *(f32x4*)(orow + d) = f32x4{o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv};
 }
 
 }  // namespace
@@ -107,7 +113,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
 hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, hipStream_t stream) {
     PrefillArgs args = a;
     args.n_qtiles = (a.q_len + kRows - 1) / kRows;
-    dim3 grid(args.n_qtiles, a.q_heads, a.batch), block(64);
+    dim3 grid(args.n_qtiles, a.q_heads, a.batch), block(kRows * kLpr);
     switch (head_dim) {
         case 32: hipLaunchKernelGGL(prefill_f32_kernel<32>, grid, block, 0, stream, args); break;
         case 64: hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, block, 0, stream, args); break;
