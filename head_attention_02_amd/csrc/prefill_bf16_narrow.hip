@@ -56,20 +56,17 @@ struct Prefill {
 
     // ---- per-lane constants ---------------------------------------------------------
     int lane, wave, g;
-    int kvalid;                 // valid key rows of this item
     int kv_rs;                  // elements from one K/V row to the next
-    const char* kg;             // K rows of this (item, kv head)
-    const char* vg;
     uint32_t k_lds0, v_lds0;    // LDS byte addresses of buffer 0
     uint32_t koff[G::NKW];      // byte offsets of this lane's K copy chunks inside a tile
     uint32_t voff;              // ... V (first copy; copy ii reads v_step * ii bytes further)
     size_t v_step;              // byte distance between the rows of consecutive V copies
     int k_read;                 // LDS byte offset of this lane's K operand (row l%32, chunk g)
     int v_read[G::DB];          // LDS byte offsets of this lane's transposing V reads
+    // the q-tile whose scores the next Q.K^T produces (its mask)
     int lo_r[RB], hi_r[RB];     // this lane's key interval, per row block
     bool blk_all_rows_valid[RB];
     int b_inter_lo[RB], b_inter_hi[RB];  // keys every row of a row block sees
-    int union_lo, union_hi;     // keys some row of the wave sees (a superset; empty if hi < lo)
     float c2;                   // scale * log2(e)
 
     // ---- running state ----------------------------------------------------------------
@@ -80,7 +77,8 @@ struct Prefill {
     // Tile copies (addresses from plan::narrow_k_chunk / narrow_v_chunk).  The tail case
     // (rows past the valid length repeat the last valid row, clamped from the tile base) is
     // decided once per tile; whole tiles use the precomputed per-lane offsets.
-    __device__ __forceinline__ void copy_k(int kt, int par) {
+    // kg / vg: K / V rows of the tile's (item, kv head); kvalid: its valid keys.
+    __device__ __forceinline__ void copy_k(const char* kg, int kvalid, int kt, int par) {
         const char* base = kg + (size_t)kt * kBN * kv_rs * 2;
         const uint32_t lds = k_lds0 + par * G::K_BYTES + wave * 1024;
         if (kt * kBN + kBN <= kvalid) {
@@ -102,7 +100,7 @@ struct Prefill {
         }
     }
 
-    __device__ __forceinline__ void copy_v(int kt, int par) {
+    __device__ __forceinline__ void copy_v(const char* vg, int kvalid, int kt, int par) {
         const char* base = vg + (size_t)kt * kBN * kv_rs * 2;
         const uint32_t lds = v_lds0 + par * G::V_BYTES + wave * 1024;
         if (kt * kBN + kBN <= kvalid) {
@@ -163,7 +161,7 @@ struct Prefill {
         pf[rb][c4] = __builtin_bit_cast(bf16x8, w);
     }
 
-    // S^T = K_tile . Q^T for every row block (the first tile, before the loop).
+    // S^T = K_tile . Q^T for every row block (no softmax work to interleave).
     __device__ __forceinline__ void qk(f32x16 (&s)[RB][2], const lds_char* kbuf) const {
 #pragma unroll
         for (int f = 0; f < 2 * G::KC; ++f) {
@@ -175,15 +173,12 @@ struct Prefill {
         }
     }
 
-    // First half of a pipelined step, as one explicitly ordered stream: the Q.K^T MFMAs
-    // of the next tile (each K operand read from LDS four steps ahead of its use and
-    // shared by all row blocks) with a slice of this tile's softmax after each of them.
-    // sched_barrier(0) keeps the compiler from regrouping the MFMAs.
-    // Whether key tile kt holds a key that some row of this wave sees.  A tile that holds
-    // none (outside the band, past the causal diagonal) takes no MFMA and no softmax work
-    // in this wave; the other waves of the workgroup may still need it.
-    __device__ __forceinline__ bool wave_sees(int kt) const {
-        return kt * kBN <= union_hi && kt * kBN + kBN - 1 >= union_lo;
+    // Whether key tile kt holds a key of uni, the keys some row of this wave sees in a
+    // q-tile.  A tile that holds none (outside the band, past the causal diagonal) takes no
+    // MFMA and no softmax work in this wave; the other waves of the workgroup may still
+    // need it.
+    static __device__ __forceinline__ bool wave_sees(plan::Keys uni, int kt) {
+        return kt * kBN <= uni.hi && kt * kBN + kBN - 1 >= uni.lo;
     }
 
     // The two halves of a step when only one of them has work in this wave.
@@ -200,6 +195,10 @@ struct Prefill {
         for (int rb = 0; rb < RB; ++rb) l_run[rb] += ls[rb][0] + ls[rb][1];
     }
 
+    // First half of a pipelined step, as one explicitly ordered stream: the Q.K^T MFMAs
+    // of the next tile (each K operand read from LDS four steps ahead of its use and
+    // shared by all row blocks) with a slice of this tile's softmax after each of them.
+    // sched_barrier(0) keeps the compiler from regrouping the MFMAs.
     template <bool HAS_NEXT>
     __device__ __forceinline__ void qk_next_probs(f32x16 (&nxt)[RB][2], const f32x16 (&cur)[RB][2],
                                                   bf16x8 (&pf)[RB][4], const lds_char* kbuf) {
@@ -288,9 +287,8 @@ struct Prefill {
         }
     }
 
-    // Row max of a whole (masked) score tile, then the running-max update.
-    __device__ __forceinline__ void update_max(const f32x16 (&s)[RB][2]) {
-        float mx[RB];
+    // Per-lane partial row max of a whole (masked) score tile (finish_max completes it).
+    __device__ __forceinline__ void row_max(const f32x16 (&s)[RB][2], float (&mx)[RB]) const {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             mx[rb] = kNegInf;
@@ -299,19 +297,17 @@ struct Prefill {
 #pragma unroll
                 for (int e = 0; e < 16; e += 2) mx[rb] = max3(mx[rb], s[rb][kb2][e], s[rb][kb2][e + 1]);
         }
-        finish_max(mx);
     }
 
     // Second half of a pipelined step: this tile's P.V MFMAs (each V^T operand read two
     // steps ahead and shared by all row blocks) with a slice of the next tile's row max
-    // after each of them; then the running-max update for the next tile.
+    // after each of them (per lane, in mx; finish_max turns it into the running-max update).
     template <bool HAS_NEXT>
     __device__ __forceinline__ void pv_max_next(const bf16x8 (&pf)[RB][4], const lds_char* vbuf,
-                                                const f32x16 (&nxt)[RB][2]) {
+                                                const f32x16 (&nxt)[RB][2], float (&mx)[RB]) {
         constexpr int NJ = 4 * G::DB;   // V^T operands per tile
         constexpr int NP = 16 * RB;     // max3 steps of the next tile
         constexpr int PF = 2;           // V^T operands in flight
-        float mx[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) mx[rb] = kNegInf;
         bf16x8 vf[PF];
@@ -334,7 +330,6 @@ struct Prefill {
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (HAS_NEXT) finish_max(mx);
     }
 };
 
@@ -350,18 +345,88 @@ struct Cfg {
     static constexpr int MINB = 2;
 };
 
+// One q-tile of a workgroup's list (in LDS): where its rows live and which key tiles it
+// visits.  kind 0: key tiles [kt_begin, kt_end) to visit; 1: rows that see no key (written
+// as zeros).
+struct TileEnt {
+    unsigned long long q_base, kv_base;   // element offsets of row 0 (plan::Rows)
+    int q0, q_len, kvalid, kt_begin, kt_end, kind;
+};
+
+constexpr int kMaxList = 64;   // q-tiles one workgroup takes at most
+
+// A position in a workgroup's stream of key tiles: list entry e, key tile kt of it (the
+// entry's end kt_end, K/V rows kv_base and valid keys cached in scalar registers).
+struct Cursor {
+    int e, kt, kt_end, kvalid;
+    unsigned long long kv_base;
+    bool valid, first;   // first: kt is the entry's first key tile
+};
+
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ unsigned long long uni64(unsigned long long x) {
+    return (unsigned long long)(unsigned)uni((int)(unsigned)x) |
+           ((unsigned long long)(unsigned)uni((int)(unsigned)(x >> 32)) << 32);
+}
+
+// Exclusive prefix sum of x over the 64 lanes of the wave; total: the sum over all.
+__device__ __forceinline__ long wave_excl_scan(long x, int lane, long& total) {
+    long inc = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const long y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+    }
+    total = __shfl(inc, 63);
+    return inc - x;
+}
+
+__device__ __forceinline__ Cursor cursor_at(const TileEnt* ents, int e, int n) {
+    Cursor c{};
+    c.e = e;
+    c.valid = e < n;
+    if (c.valid) {
+        c.kt = uni(ents[e].kt_begin);
+        c.kt_end = uni(ents[e].kt_end);
+        c.kvalid = uni(ents[e].kvalid);
+        c.kv_base = uni64(ents[e].kv_base);
+        c.first = true;
+    }
+    return c;
+}
+
+__device__ __forceinline__ Cursor advance(Cursor c, const TileEnt* ents, int n) {
+    if (!c.valid) return c;
+    if (c.kt + 1 < c.kt_end) {
+        ++c.kt;
+        c.first = false;
+        return c;
+    }
+    return cursor_at(ents, c.e + 1, n);
+}
+
 // GATE: waves skip the work of key tiles none of their rows sees.  Only causal and banded
 // launches have such tiles; the full bidirectional launch keeps the ungated stream, whose
 // schedule the extra branches would only disturb (measured 39.9 vs 41.3 us on the padded
 // BERT batch, both timed in the kernel's form for a non-positive scale).
+//
+// Persistent: each workgroup walks the list of q-tiles plan::persist_pos deals it and runs
+// their key tiles as one pipelined stream (the key tiles of the next q-tile follow those
+// of the current one without a pause: its Q rows are loaded one step ahead of its first
+// Q.K^T, its first K/V tiles are copied as any other), so that only the first q-tile of a
+// workgroup waits for its start-up loads.
 template <int D, bool POS_SCALE, bool GATE, bool F16>
 __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_narrow_kernel(PrefillArgs a) {
     constexpr int RB = Cfg<D>::RB;
     constexpr int W = Cfg<D>::W;
     constexpr int BM = Cfg<D>::BM;
+    static_assert(RB == 1, "one row block per wave");
     using G = Geo<D, W>;
     __shared__ __attribute__((aligned(16))) u32x4 k_lds[2][kBN * G::KS];
     __shared__ __attribute__((aligned(16))) u32x4 v_lds[2][kBN * G::CPR];
+    __shared__ __attribute__((aligned(16))) u32x4 q_lds[W * G::KC * 64];   // next q-tile's Q^T operands
+    __shared__ TileEnt ents[kMaxList];
+    __shared__ int s_counts[3];   // entries with key tiles, entries of zero rows, key tiles in all
 
     Prefill<D, RB, W, POS_SCALE, F16> st;
     using H = Fmt16<F16>;
@@ -373,73 +438,145 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
     st.lane = lane;
     st.wave = wave;
     st.g = g;
-    // block -> (q-tile, item, head): longest tiles first, XCD-aware (plan::map_block)
-    const plan::BlockCoord bc = plan::map_block(blockIdx.x, a.n_qtiles, a.batch, a.q_heads, a.kv_heads,
-                                                last_tiles_first(a), kXcds);
-    const int qt = bc.qt, b = bc.b, h = bc.h;
-    const int grp = a.q_heads / a.kv_heads;
-    const int kvh = h / grp;
+    const bool causal = a.causal != 0;
+    // row strides of q / out and of k / v (plan::item_rows: token-major and unpadded
+    // layouts interleave the heads of a token)
+    const int q_rs = (a.cu_seqlens != nullptr || a.token_major) ? a.q_heads * D : D;
+    st.kv_rs = (a.cu_seqlens != nullptr || a.token_major) ? a.kv_heads * D : D;
 
-    const plan::Rows ir = item_rows(a, b, h, kvh, D);
-    const int valid = ir.kv_valid;
-    const int q_len = ir.q_len;
-    st.kvalid = valid;
-    st.kv_rs = ir.kv_rs;
-
-    const int q0 = qt * BM;
-    if (q0 >= q_len) return;   // no query row of this item in the tile (unpadded layout)
-    const int last_row = min(q0 + BM, q_len) - 1;
-
-    // ---- key tiles of the whole workgroup: the union of its rows' key sets -------------
-    const plan::Tiles tiles = plan::key_tiles(
-        plan::span_union(a.pos_offset + q0, a.pos_offset + last_row, valid, a.causal != 0, a.window), kBN);
-    const int kt_begin = tiles.begin;
-    const int kt_end = tiles.end;
-
-    // ---- per row block: this lane's query row and key interval, the block's common keys
-    int my_row[RB];
+    // ---- this workgroup's q-tiles: lane k of wave 0 looks up the k-th ------------------
+    // (plan::persist_pos; with per-item lengths for at most kRankedItems items, in the
+    // ranked order of plan::ranked_tile)
+    __shared__ int s_order[plan::kRankedItems], s_ne[plan::kRankedItems], s_nrow[plan::kRankedItems];
+    __shared__ int s_i0[plan::kRankedItems], s_i1[plan::kRankedItems];
+    __shared__ long s_start_ne[plan::kRankedItems], s_start_z[plan::kRankedItems];
+    const bool has_len = a.seq_lens != nullptr || a.cu_seqlens != nullptr;
+    const bool ranked = has_len && a.batch <= plan::kRankedItems;
+    if (wave == 0) {
+        const long pk = plan::persist_pos((int)blockIdx.x, lane, (int)gridDim.x, kXcds);
+        bool have = false;
+        int b = 0, h = 0, qt = 0;
+        plan::Rows ir{};
+        if (ranked) {
+            // lane b: item b's rows, keys and schedule numbers; its rank by cost
+            const int B = a.batch;
+            int i0 = 0, i1 = 0, rows = 0, valid = 0;
+            if (lane < B) {
+                if (a.cu_seqlens) {
+                    i0 = a.cu_seqlens[lane];
+                    i1 = a.cu_seqlens[lane + 1];
+                    rows = min(max(i1 - i0, 0), a.q_len);
+                    valid = rows;
+                } else {
+                    i0 = a.seq_lens[lane];
+                    rows = a.q_len;
+                    valid = min(max(i0, 0), a.kv_len);
+                }
+            }
+            const plan::ItemSched is = lane < B ? plan::item_sched(rows, valid, a.pos_offset, causal, a.window, BM, kBN)
+                                                : plan::ItemSched{0, 0, -1};
+            int rank = 0;
+            for (int x = 0; x < B; ++x)
+                rank += plan::ranks_before(__builtin_amdgcn_readlane(is.cost, x), x, is.cost, lane) ? 1 : 0;
+            if (lane < B) {
+                s_order[rank] = lane;
+                s_ne[lane] = is.ne;
+                s_nrow[lane] = is.nrow;
+                s_i0[lane] = i0;
+                s_i1[lane] = i1;
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the writes have landed
+            __builtin_amdgcn_wave_barrier();
+            const long tiles_r = lane < B ? (long)s_ne[s_order[lane]] * a.q_heads : 0;   // q-tiles of rank lane
+            const long zeros_b = lane < B ? (long)(is.nrow - is.ne) * a.q_heads : 0;
+            long n_ne = 0, n_z = 0;
+            const long x_ne = wave_excl_scan(tiles_r, lane, n_ne);
+            const long x_z = wave_excl_scan(zeros_b, lane, n_z);
+            if (lane < B) {
+                s_start_ne[lane] = x_ne;
+                s_start_z[lane] = x_z;
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();
+            typedef __attribute__((address_space(3))) const int lds_int;
+            typedef __attribute__((address_space(3))) const long lds_long;
+            const plan::RankedRef rr = plan::ranked_tile(pk, B, a.q_heads, n_ne, n_z, (lds_int*)s_order,
+                                                         (lds_long*)s_start_ne, (lds_long*)s_start_z,
+                                                         (lds_int*)s_ne, (lds_int*)s_nrow);
+            if (rr.kind != 2) {
+                have = true;
+                b = rr.b;
+                h = rr.h;
+                qt = rr.qt;
+                const plan::Layout lay = a.cu_seqlens ? plan::kUnpadded : a.token_major ? plan::kTokenMajor : plan::kHeadMajor;
+                ir = plan::item_rows(lay, b, h, h / (a.q_heads / a.kv_heads), D, a.q_heads, a.kv_heads, a.q_len,
+                                     a.kv_len, s_i0[b], s_i1[b], a.seq_lens != nullptr, s_i0[b]);
+            }
+        } else if (pk < (long)a.batch * a.q_heads * a.n_qtiles) {
+            const plan::TileRef t = plan::persist_tile(pk, a.q_heads, a.n_qtiles);
+            have = true;
+            b = t.b;
+            h = t.h;
+            qt = t.qt;
+            ir = item_rows(a, b, h, h / (a.q_heads / a.kv_heads), D);
+        }
+        TileEnt e{};
+        int kind = 2;   // no q-tile (past the list, or no rows in it)
+        if (have) {
+            const int q0 = qt * BM;
+            if (q0 < ir.q_len) {
+                const int last = min(q0 + BM, ir.q_len) - 1;
+                const plan::Tiles kt = plan::key_tiles(
+                    plan::span_union(a.pos_offset + q0, a.pos_offset + last, ir.kv_valid, causal, a.window), kBN);
+                e.q_base = ir.q_base;
+                e.kv_base = ir.kv_base;
+                e.q0 = q0;
+                e.q_len = ir.q_len;
+                e.kvalid = ir.kv_valid;
+                e.kt_begin = kt.begin;
+                e.kt_end = kt.end;
+                kind = kt.end > kt.begin ? 0 : 1;
+                e.kind = kind;
+            }
+        }
+        const unsigned long long m0 = __builtin_amdgcn_ballot_w64(kind == 0);
+        const unsigned long long m1 = __builtin_amdgcn_ballot_w64(kind == 1);
+        const unsigned long long below = (1ull << lane) - 1ull;
+        const int n0 = __builtin_popcountll(m0);
+        if (kind == 0) ents[__builtin_popcountll(m0 & below)] = e;
+        if (kind == 1) ents[n0 + __builtin_popcountll(m1 & below)] = e;
+        int steps = kind == 0 ? e.kt_end - e.kt_begin : 0;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int r0 = q0 + (wave * RB + rb) * 32;
-        my_row[rb] = r0 + (lane & 31);
-        const RowBlockKeys k = row_block_keys(a, r0, 32, my_row[rb], q_len, valid);
-        st.lo_r[rb] = k.lane.lo;
-        st.hi_r[rb] = k.lane.hi;
-        st.b_inter_lo[rb] = k.inter.lo;
-        st.b_inter_hi[rb] = k.inter.hi;
-        st.blk_all_rows_valid[rb] = k.all_rows_valid;
-    }
-    {   // the union of the key intervals of the wave's rows (all its row blocks)
-        const int r0 = q0 + wave * RB * 32;
-        const RowBlockKeys k = row_block_keys(a, r0, RB * 32, r0, q_len, valid);
-        st.union_lo = k.uni.lo;
-        st.union_hi = k.uni.hi;
-    }
-
-    // ---- Q^T operands: lane l holds row l%32 of each block, dims 16*kc + 8*g + [0, 8)
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const uint16_t* qrow = (const uint16_t*)a.q + ir.q_base + (size_t)min(my_row[rb], q_len - 1) * ir.q_rs;
-        const bool in = my_row[rb] < q_len;
-#pragma unroll
-        for (int kc = 0; kc < G::KC; ++kc) {
-            u32x4 w = in ? *(const u32x4*)(qrow + 16 * kc + 8 * g) : u32x4{0, 0, 0, 0};
-            st.qf[rb][kc] = __builtin_bit_cast(bf16x8, w);
+        for (int o = 32; o >= 1; o >>= 1) steps += __shfl_xor(steps, o);
+        if (lane == 0) {
+            s_counts[0] = n0;
+            s_counts[1] = __builtin_popcountll(m1);
+            s_counts[2] = steps;
         }
     }
-    // Q is waited for in the prologue below, together with the first tile copies (one
-    // memory latency instead of several).  That explicit wait also keeps the compiler from
-    // placing its own wait for Q inside the loop, where it would also wait for the next
-    // tile's copy.
+    __syncthreads();
+    const int n_ent = uni(s_counts[0]);
+    const int n_zero = uni(s_counts[1]);
+    const int n_steps = uni(s_counts[2]);
 
-    st.kg = (const char*)((const uint16_t*)a.k + ir.kv_base);
-    st.vg = (const char*)((const uint16_t*)a.v + ir.kv_base);
+    // q-tiles whose rows see no key (padded rows, queries past the keys): zeros
+    for (int z = 0; z < n_zero; ++z) {
+        const TileEnt& t = ents[n_ent + z];
+        const int rows = min(BM, uni(t.q_len) - uni(t.q0));
+        uint16_t* o0 = (uint16_t*)a.out + uni64(t.q_base) + (size_t)uni(t.q0) * q_rs;
+        for (int i = tid; i < rows * (D / 8); i += W * 64)
+            *(u32x4*)(o0 + (size_t)(i / (D / 8)) * q_rs + 8 * (i % (D / 8))) = u32x4{0, 0, 0, 0};
+    }
+    if (n_ent == 0) return;
+
+    // ---- per-lane constants ---------------------------------------------------------------
     st.k_lds0 = lds_addr(k_lds[0]);
     st.v_lds0 = lds_addr(v_lds[0]);
 #pragma unroll
-    for (int ii = 0; ii < G::NKW; ++ii) st.koff[ii] = plan::chunk_offset(plan::narrow_k_chunk(wave + W * ii, lane, G::CPR), ir.kv_rs);
-    st.voff = plan::chunk_offset(plan::narrow_v_chunk(wave, lane, D), ir.kv_rs);
-    st.v_step = plan::narrow_v_copy_step(W, D, ir.kv_rs);
+    for (int ii = 0; ii < G::NKW; ++ii)
+        st.koff[ii] = plan::chunk_offset(plan::narrow_k_chunk(wave + W * ii, lane, G::CPR), st.kv_rs);
+    st.voff = plan::chunk_offset(plan::narrow_v_chunk(wave, lane, D), st.kv_rs);
+    st.v_step = plan::narrow_v_copy_step(W, D, st.kv_rs);
     st.k_read = ((lane & 31) * G::KS + g) * 16;
     {
         const int r = 4 * g + ((lane & 15) >> 2);
@@ -450,109 +587,212 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
         }
     }
     st.c2 = a.scale * kLog2e;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-        for (int i = 0; i < G::DB; ++i) st.o[rb][i] = f32x16{};
-        st.m_run[rb] = kNegInf;   // running (possibly stale) max of this lane's row, log2 units
-        st.l_run[rb] = 0.0f;      // running sum over this lane's half of the keys
-    }
+    const char* kg0 = (const char*)a.k;
+    const char* vg0 = (const char*)a.v;
+    auto kg_of = [&](const Cursor& c) { return kg0 + 2 * c.kv_base; };
+    auto vg_of = [&](const Cursor& c) { return vg0 + 2 * c.kv_base; };
 
-    const lds_char* kb[2] = {(const lds_char*)(const void*)k_lds[0], (const lds_char*)(const void*)k_lds[1]};
-    const lds_char* vb[2] = {(const lds_char*)(const void*)v_lds[0], (const lds_char*)(const void*)v_lds[1]};
-
-    // One pipelined step for tile kt = kt_begin + j (buffer parity PAR = j & 1): cur holds
-    // the masked scores of tile kt with the running max already updated for it.
-    auto step = [&](auto has_next_c, auto par_c, f32x16 (&cur)[RB][2], f32x16 (&nxt)[RB][2], int j) {
-        constexpr bool HAS_NEXT = decltype(has_next_c)::value;
-        constexpr int PAR = decltype(par_c)::value;
-        const int kt = kt_begin + j;
-        wait_vm0();          // this thread's copies of K(kt+1) and V(kt) have landed
-        __syncthreads();     // ... everyone's; and nobody still reads K(kt) or V(kt-1)
-        if (kt + 2 < kt_end) st.copy_k(kt + 2, PAR);
-        if (HAS_NEXT) st.copy_v(kt + 1, PAR ^ 1);
-        bf16x8 pf[RB][4];
-        // Wave-uniform: whether this wave has rows that see tile kt (its softmax and P.V)
-        // and tile kt+1 (its Q.K^T, mask and max).
-        const bool see_cur = !GATE || st.wave_sees(kt);
-        const bool see_nxt = HAS_NEXT && (!GATE || st.wave_sees(kt + 1));
-        if (!GATE || (see_cur && see_nxt)) {
-            st.template qk_next_probs<HAS_NEXT>(nxt, cur, pf, kb[PAR ^ 1]);
-            if (HAS_NEXT) st.mask_scale(nxt, kt + 1);
-            st.template pv_max_next<HAS_NEXT>(pf, vb[PAR], nxt);
-        } else if (see_cur && see_nxt) {
-            st.template qk_next_probs<true>(nxt, cur, pf, kb[PAR ^ 1]);
-            st.mask_scale(nxt, kt + 1);
-            st.template pv_max_next<true>(pf, vb[PAR], nxt);
-        } else if (see_cur) {
-            keep_branch();
-            st.probs_only(cur, pf);
-            st.template pv_max_next<false>(pf, vb[PAR], nxt);
-        } else if (see_nxt) {
-            keep_branch();
-            st.qk(nxt, kb[PAR ^ 1]);
-            st.mask_scale(nxt, kt + 1);
-            st.update_max(nxt);
-        }
+    // Q^T operands of entry e's rows for this wave: lane l holds row l%32, dims
+    // 16*kc + 8*g + [0, 8).  Rows past the end read the last row (their keys are masked
+    // and their output is not stored).  load_q reads them into registers (the first
+    // q-tile); copy_q copies them into this wave's part of q_lds (1 KiB per k-step, lane l's
+    // 16 bytes at 16*l), and read_q moves them into registers once the copy has landed.
+    auto load_q = [&](bf16x8 (&qf)[G::KC], int e) {
+        const int q0 = uni(ents[e].q0), q_len = uni(ents[e].q_len);
+        const uint16_t* qrow = (const uint16_t*)a.q + uni64(ents[e].q_base) +
+                               (size_t)min(q0 + wave * 32 + (lane & 31), q_len - 1) * q_rs;
+#pragma unroll
+        for (int kc = 0; kc < G::KC; ++kc)
+            qf[kc] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * kc + 8 * g));
     };
-
-    const int n = kt_end - kt_begin;
-    if (n > 0) {
-        f32x16 sa[RB][2], sb[RB][2];
-        st.copy_k(kt_begin, 0);
-        if (n > 1) st.copy_k(kt_begin + 1, 1);
-        st.copy_v(kt_begin, 0);
-        wait_vm0();          // Q, K(0), K(1) and V(0) have landed
-        __syncthreads();
-        if (!GATE || st.wave_sees(kt_begin)) {
-            st.qk(sa, kb[0]);
-            st.mask_scale(sa, kt_begin);
-            st.update_max(sa);
-        }
-        typedef std::integral_constant<bool, true> T_;
-        typedef std::integral_constant<bool, false> F_;
-        typedef std::integral_constant<int, 0> P0;
-        typedef std::integral_constant<int, 1> P1;
-        int j = 0;
-        for (; j + 2 < n; j += 2) {
-            step(T_{}, P0{}, sa, sb, j);
-            step(T_{}, P1{}, sb, sa, j + 1);
-        }
-        if (j + 1 < n) {
-            step(T_{}, P0{}, sa, sb, j);
-            step(F_{}, P1{}, sb, sa, j + 1);
-        } else {
-            step(F_{}, P0{}, sa, sb, j);
-        }
-    }
-
-    // ---- epilogue: normalise, zero padded / empty rows, store bf16 --------------------
+    const uint32_t q_lds0 = lds_addr(q_lds) + wave * G::KC * 1024;
+    auto copy_q = [&](int e) {
+        const int q0 = uni(ents[e].q0), q_len = uni(ents[e].q_len);
+        const int rb = min(q0 + wave * 32, q_len - 1);   // the wave's first row, clamped
+        const char* src = (const char*)((const uint16_t*)a.q + uni64(ents[e].q_base) + (size_t)rb * q_rs);
+        const uint32_t voff = plan::q_copy_offset(min(q0 + wave * 32 + (lane & 31), q_len - 1) - rb, g, q_rs);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const float l_tot = halves_sum(st.l_run[rb]);
-        if (my_row[rb] < q_len) {
-            const float inv = (st.hi_r[rb] >= 0 && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
-            uint16_t* orow = (uint16_t*)a.out + ir.q_base + (size_t)my_row[rb] * ir.q_rs;
+        for (int kc = 0; kc < G::KC; ++kc) lds_dma16(src, voff + 32 * kc, q_lds0 + kc * 1024);
+    };
+    auto read_q = [&](bf16x8 (&qf)[G::KC]) {
+        const lds_char* p = (const lds_char*)(const void*)q_lds + (wave * G::KC * 1024 + lane * 16);
+#pragma unroll
+        for (int kc = 0; kc < G::KC; ++kc) qf[kc] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(p + kc * 1024));
+    };
+    // The rows of entry e as the next Q.K^T's mask and gate see them.
+    auto set_rows = [&](int e) {
+        const int q0 = uni(ents[e].q0), q_len = uni(ents[e].q_len), kvalid = uni(ents[e].kvalid);
+        const int r0 = q0 + wave * 32;
+        const RowBlockKeys k = row_block_keys(a, r0, 32, r0 + (lane & 31), q_len, kvalid);
+        st.lo_r[0] = k.lane.lo;
+        st.hi_r[0] = k.lane.hi;
+        st.b_inter_lo[0] = k.inter.lo;
+        st.b_inter_hi[0] = k.inter.hi;
+        st.blk_all_rows_valid[0] = k.all_rows_valid;
+        return plan::Keys{uni(k.uni.lo), uni(k.uni.hi)};
+    };
+    // Output of entry e: O / l, zero for rows that see no key, stored with RNE; then the
+    // softmax state starts afresh.  Returns whether every row of the wave was stored (then
+    // the stores are exactly kStores instructions).
+    constexpr int kStores = G::DB * 4;
+    auto finish_tile = [&](int e) {
+        const int q0 = uni(ents[e].q0), q_len = uni(ents[e].q_len), kvalid = uni(ents[e].kvalid);
+        const int row = q0 + wave * 32 + (lane & 31);
+        const float l_tot = halves_sum(st.l_run[0]);
+        const bool sees = plan::row_keys(a.pos_offset + row, kvalid, causal, a.window).hi >= 0;
+        const float inv = (sees && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
+        uint16_t* orow = (uint16_t*)a.out + uni64(ents[e].q_base) + (size_t)min(row, q_len - 1) * q_rs;
+        const bool full = q0 + wave * 32 + 32 <= q_len;
+        if (full || row < q_len) {
 #pragma unroll
             for (int db = 0; db < G::DB; ++db) {
 #pragma unroll
                 for (int e4 = 0; e4 < 4; ++e4) {
                     const int d = 32 * db + 8 * e4 + 4 * g;
                     u32x2 w;
-                    w[0] = H::pack2(st.o[rb][db][4 * e4] * inv, st.o[rb][db][4 * e4 + 1] * inv);
-                    w[1] = H::pack2(st.o[rb][db][4 * e4 + 2] * inv, st.o[rb][db][4 * e4 + 3] * inv);
+                    w[0] = H::pack2(st.o[0][db][4 * e4] * inv, st.o[0][db][4 * e4 + 1] * inv);
+                    w[1] = H::pack2(st.o[0][db][4 * e4 + 2] * inv, st.o[0][db][4 * e4 + 3] * inv);
                     *(u32x2*)(orow + d) = w;
                 }
             }
         }
+#pragma unroll
+        for (int i = 0; i < G::DB; ++i) st.o[0][i] = f32x16{};
+        st.m_run[0] = kNegInf;
+        st.l_run[0] = 0.0f;
+        return full;
+    };
+
+    const lds_char* kb[2] = {(const lds_char*)(const void*)k_lds[0], (const lds_char*)(const void*)k_lds[1]};
+    const lds_char* vb[2] = {(const lds_char*)(const void*)v_lds[0], (const lds_char*)(const void*)v_lds[1]};
+
+    // ---- the stream: step s computes the softmax and P.V of key tile s and the Q.K^T of
+    // key tile s+1; it copies K(s+2) and V(s+1) (cursors cur, nv, nk) --------------------
+    Cursor cur{}, nv = cursor_at(ents, 0, n_ent), nk = advance(nv, ents, n_ent);
+    load_q(st.qf[0], 0);
+    if (nk.valid && nk.first) copy_q(nk.e);
+    plan::Keys uni_nxt = set_rows(0), uni_cur{0, -1};
+#pragma unroll
+    for (int i = 0; i < G::DB; ++i) st.o[0][i] = f32x16{};
+    st.m_run[0] = kNegInf;   // running (possibly stale) max of this lane's row, log2 units
+    st.l_run[0] = 0.0f;      // running sum over this lane's half of the keys
+    bool stores_pending = false;
+
+    f32x16 sa[RB][2], sb[RB][2];
+    st.copy_k(kg_of(nv), nv.kvalid, nv.kt, 0);
+    if (nk.valid) st.copy_k(kg_of(nk), nk.kvalid, nk.kt, 1);
+    st.copy_v(vg_of(nv), nv.kvalid, nv.kt, 0);
+    wait_vm0();          // Q, the first K tiles and V tile have landed
+    __syncthreads();
+    if (!GATE || st.wave_sees(uni_nxt, nv.kt)) {
+        float mx[RB];
+        st.qk(sa, kb[0]);
+        st.mask_scale(sa, nv.kt);
+        st.row_max(sa, mx);
+        st.finish_max(mx);
     }
+
+    auto step = [&](auto has_next_c, auto par_c, f32x16 (&cs)[RB][2], f32x16 (&ns)[RB][2]) {
+        constexpr bool HAS_NEXT = decltype(has_next_c)::value;
+        constexpr int PAR = decltype(par_c)::value;
+        // this thread's copies of K(s+1) and V(s) (and Q rows) have landed -- the output
+        // stores of the previous step, issued after them, may stay in flight (vector memory
+        // operations of a wave complete in issue order) ...
+        if (stores_pending)
+            wait_vm<kStores>();
+        else
+            wait_vm0();
+        __syncthreads();     // ... everyone's; and nobody still reads K(s) or V(s-1)
+        cur = nv;
+        nv = nk;
+        nk = advance(nk, ents, n_ent);
+        uni_cur = uni_nxt;
+        // the next key tile starts a q-tile: its Q rows (copied a step ago) and its masks;
+        // the Q copy of the q-tile after it may then reuse q_lds
+        if (HAS_NEXT && nv.first) {
+            keep_branch();
+            read_q(st.qf[0]);
+            uni_nxt = set_rows(nv.e);
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the reads have left q_lds
+        }
+        if (nk.valid) st.copy_k(kg_of(nk), nk.kvalid, nk.kt, PAR);
+        if (HAS_NEXT) st.copy_v(vg_of(nv), nv.kvalid, nv.kt, PAR ^ 1);
+        if (nk.valid && nk.first) {
+            keep_branch();
+            copy_q(nk.e);
+        }
+        bf16x8 pf[RB][4];
+        float mx[RB];
+        // Wave-uniform: whether this wave has rows that see key tile s (its softmax and
+        // P.V) and key tile s+1 (its Q.K^T, mask and max).
+        const bool see_cur = !GATE || st.wave_sees(uni_cur, cur.kt);
+        const bool see_nxt = HAS_NEXT && (!GATE || st.wave_sees(uni_nxt, nv.kt));
+        if (!GATE || (see_cur && see_nxt)) {
+            st.template qk_next_probs<HAS_NEXT>(ns, cs, pf, kb[PAR ^ 1]);
+            if (HAS_NEXT) st.mask_scale(ns, nv.kt);
+            st.template pv_max_next<HAS_NEXT>(pf, vb[PAR], ns, mx);
+        } else if (see_cur && see_nxt) {
+            st.template qk_next_probs<true>(ns, cs, pf, kb[PAR ^ 1]);
+            st.mask_scale(ns, nv.kt);
+            st.template pv_max_next<true>(pf, vb[PAR], ns, mx);
+        } else if (see_cur) {
+            keep_branch();
+            st.probs_only(cs, pf);
+            st.template pv_max_next<false>(pf, vb[PAR], ns, mx);
+        } else if (see_nxt) {
+            keep_branch();
+            st.qk(ns, kb[PAR ^ 1]);
+            st.mask_scale(ns, nv.kt);
+            st.row_max(ns, mx);
+        }
+        // key tile s was the last of its q-tile: its output
+        stores_pending = false;
+        if (!HAS_NEXT || nv.first) {
+            keep_branch();
+            stores_pending = uni(finish_tile(cur.e)) != 0;
+        }
+        if (see_nxt) st.finish_max(mx);
+    };
+
+    typedef std::integral_constant<bool, true> T_;
+    typedef std::integral_constant<bool, false> F_;
+    typedef std::integral_constant<int, 0> P0;
+    typedef std::integral_constant<int, 1> P1;
+    int j = 0;
+    for (; j + 2 < n_steps; j += 2) {
+        step(T_{}, P0{}, sa, sb);
+        step(T_{}, P1{}, sb, sa);
+    }
+    if (j + 1 < n_steps) {
+        step(T_{}, P0{}, sa, sb);
+        step(F_{}, P1{}, sb, sa);
+    } else {
+        step(F_{}, P0{}, sa, sb);
+    }
+}
+
+// Workgroups the device holds at once (Cfg::MINB per CU), per device.
+int narrow_slots() {
+    static int slots[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (slots[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return 0;
+        slots[dev] = cus * Cfg<64>::MINB;
+    }
+    return slots[dev];
 }
 
 template <int D>
 hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
     PrefillArgs args = a;
     args.n_qtiles = (a.q_len + Cfg<D>::BM - 1) / Cfg<D>::BM;
-    const dim3 grid((unsigned)args.n_qtiles * a.q_heads * a.batch);
+    const long tiles = (long)args.n_qtiles * a.q_heads * a.batch;
+    const int slots = narrow_slots();
+    if (slots <= 0) return hipErrorInvalidDevice;
+    const dim3 grid((unsigned)plan::persist_grid(tiles, slots, kXcds, kMaxList));
     const dim3 block(Cfg<D>::THREADS);
     const bool gate = a.causal || a.window > 0;
     if (args.f16) {

@@ -45,6 +45,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // s_waitcnt vmcnt(0): every global load (tile copies included) of this wave has landed.
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt vmcnt(N): at most the N vector memory operations this wave issued last are
+// still in flight (they complete in issue order, stores included); expcnt and lgkmcnt are
+// not waited for.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // Marks a rarely taken, wave-uniform branch as having a side effect so that the compiler
 // keeps it a branch instead of computing its body on every tile and selecting.
 __device__ __forceinline__ void keep_branch() { asm volatile("" ::); }

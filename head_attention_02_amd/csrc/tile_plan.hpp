@@ -122,6 +122,120 @@ constexpr BlockCoord map_block(unsigned block, int n_qtiles, int batch, int q_he
     return {last_first ? n_qtiles - 1 - qt_rank : qt_rank, b, h};
 }
 
+// ---- persistent grid of the head-dim-32/64 kernel ------------------------------------------
+//
+// That kernel runs `wgs` workgroups (a multiple of xcds) and each walks a list of q-tiles,
+// streaming the key tiles of one q-tile after another so that the start-up latency of a
+// q-tile (its Q rows, its first K/V tiles) hides behind the work of the previous one.
+// The q-tiles (item b, query head h, q-tile qt) are numbered
+// p = (b * q_heads + h) * n_qtiles + (n_qtiles - 1 - qt), last q-tile first within a head,
+// and dealt in rounds of `wgs` numbers: round k covers [k * wgs, (k + 1) * wgs), every other
+// round in reverse order (so that a workgroup dealt an early number in one round gets a
+// late one in the next), and within a round the workgroups of XCD x (block i runs on XCD
+// i % xcds) take one contiguous block of wgs / xcds numbers, so that neighbouring q-tiles
+// of a head -- which read the same K/V tiles -- are fetched into one L2.
+constexpr int persist_slot(int wg, int wgs, int xcds) { return (wg % xcds) * (wgs / xcds) + wg / xcds; }
+
+// The number of the k-th q-tile of workgroup wg (increasing in k; the list ends at the
+// first number past the last q-tile).
+constexpr long persist_pos(int wg, int k, int wgs, int xcds) {
+    const int j = persist_slot(wg, wgs, xcds);
+    return (long)k * wgs + ((k & 1) ? wgs - 1 - j : j);
+}
+
+struct TileRef {
+    int b, h, qt;
+};
+constexpr TileRef persist_tile(long p, int q_heads, int n_qtiles) {
+    const long bh = p / n_qtiles;
+    return {(int)(bh / q_heads), (int)(bh % q_heads), n_qtiles - 1 - (int)(p % n_qtiles)};
+}
+
+// With per-item lengths (up to kRankedItems items) the numbers run over the q-tiles in
+// a ranked order instead, so that the rounds deal the costliest q-tiles first (each
+// workgroup's later, reversed rounds then bring it cheaper ones): first every q-tile that
+// visits keys -- items by the key tiles of their costliest q-tile, most first (ties by item
+// index), within an item query head by query head, last q-tile first -- then every
+// q-tile whose rows see no key (zeros to write), items in index order.
+constexpr int kRankedItems = 64;
+
+struct ItemSched {
+    int nrow;   // q-tiles holding rows of the item
+    int ne;     // ... of which the first ne hold a row that sees a key
+    int cost;   // key tiles of the item's costliest q-tile (its last non-empty one)
+};
+// rows: query rows of the item; valid: its keys; p: pos_offset.  A row r sees a key iff
+// p + r < valid (plan::row_keys), so the non-empty q-tiles are a prefix.
+constexpr ItemSched item_sched(int rows, int valid, int p, bool causal, int window, int bm, int bn) {
+    ItemSched s{};
+    s.nrow = (imax(rows, 0) + bm - 1) / bm;
+    const int seen_rows = imin(imax(rows, 0), imax(valid - p, 0));
+    s.ne = (seen_rows + bm - 1) / bm;
+    if (s.ne > 0) {
+        const int q0 = (s.ne - 1) * bm, last = imin(q0 + bm, rows) - 1;
+        const Tiles t = key_tiles(span_union(p + q0, p + last, valid, causal, window), bn);
+        s.cost = t.end - t.begin;
+    }
+    return s;
+}
+
+// Whether item a (cost_a) ranks before item b (cost_b).
+constexpr bool ranks_before(int cost_a, int a, int cost_b, int b) { return cost_a > cost_b || (cost_a == cost_b && a < b); }
+
+// The last index i in [0, n) with a[i] <= x (a non-decreasing, a[0] <= x).  P: a pointer
+// or array-like type (the kernel passes LDS pointers).
+template <class P>
+constexpr int last_at_most(P a, int n, long x) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (a[mid] <= x)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// Number p of the ranked order -> q-tile.  order[r]: the item of rank r; start_ne[r]: the
+// number of its first non-empty q-tile (n_ne in all); start_z[b]: the number of item b's
+// first zero q-tile, counted from n_ne (n_z in all).  kind 0: a q-tile with keys, 1: zeros,
+// 2: past the end.
+struct RankedRef {
+    int b, h, qt, kind;
+};
+template <class IP, class LP>
+constexpr RankedRef ranked_tile(long p, int items, int q_heads, long n_ne, long n_z, IP order, LP start_ne,
+                                LP start_z, IP ne, IP nrow) {
+    RankedRef t{0, 0, 0, 2};
+    if (p < n_ne) {
+        const int r = last_at_most(start_ne, items, p);
+        const int b = order[r];
+        const long local = p - start_ne[r];
+        t = {b, (int)(local / ne[b]), ne[b] - 1 - (int)(local % ne[b]), 0};
+    } else if (p < n_ne + n_z) {
+        const long pz = p - n_ne;
+        const int b = last_at_most(start_z, items, pz);
+        const int nz = nrow[b] - ne[b];
+        const long local = pz - start_z[b];
+        t = {b, (int)(local / nz), ne[b] + (int)(local % nz), 1};
+    }
+    return t;
+}
+
+// Grid size: the `slots` workgroups that fit on the device at once (rounded down to a
+// multiple of xcds), no more than `tiles` needs, and enough that no list is longer than
+// max_list.
+constexpr int persist_grid(long tiles, int slots, int xcds, int max_list) {
+    long g = (long)slots / xcds * xcds;
+    const long need = (tiles + xcds - 1) / xcds * xcds;
+    if (g > need) g = need;
+    const long min_g = ((tiles + max_list - 1) / max_list + xcds - 1) / xcds * xcds;
+    if (g < min_g) g = min_g;
+    if (g < xcds) g = xcds;
+    return (int)g;
+}
+
 // ---- where an item's rows live ---------------------------------------------------------
 
 // Layouts of the prefill tensors.
@@ -278,6 +392,12 @@ constexpr Chunk narrow_v_chunk(int i, int lane, int D) {
 // narrow_v_chunk(w + waves*ii, ...), which is wave w's copy 0 moved down by
 // waves*64/cpr rows (a whole number of swizzle periods), i.e. this many bytes further.
 constexpr size_t narrow_v_copy_step(int waves, int D, int kv_rs) { return (size_t)(waves * 64 / (D / 8)) * kv_rs * 2; }
+
+// Q copy of the head-dim-32/64 kernel (a q-tile's rows copied ahead of its first Q.K^T):
+// lane p reads query row r + p%32 (rows past the end clamped to the last; `row` is that
+// row relative to the wave's first, clamped the same way) at elements 8*(p/32) + 16*kc,
+// copy kc adding 32*kc bytes to this offset.
+constexpr uint32_t q_copy_offset(int row, int half, int q_rs) { return (uint32_t)((row * q_rs + 8 * half) * 2); }
 
 // ---- decode launch plan --------------------------------------------------------------------
 

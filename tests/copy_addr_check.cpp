@@ -7,13 +7,14 @@
 //       the longest); D 32/64 run the narrow kernel's plan, 128 the wide kernel's.
 //   decode MODE B Hq Hkv CAP KV_LEN D P W NLENS len_0 ..
 //       MODE 0 stacked caches, 1 per-item caches, 2 per-item with append.
-// For every block of the grid it enumerates every tile a workgroup visits, every copy
+// For every block of the grid (the head-dim-32/64 kernel: every workgroup of its
+// persistent grid and every q-tile of its list) it enumerates every tile visited, every copy
 // instruction and every lane, computes the byte offset exactly as the kernel does (whole
 // tiles: per-copy base + per-lane offset; tail tiles: rows clamped from the tile base),
 // and checks that the 16 bytes lie inside the item's valid rows [0, kvalid) and columns
 // [0, D), inside the tensor, and that the LDS destination lies inside the tile buffers.
-// It also checks that the grid's block -> (q-tile, item, head) map is a bijection, and
-// the Q and output row addresses.  Decode: every cache row a lane reads lies in the
+// It also checks that the grid covers every (q-tile, item, head) exactly once, and the Q
+// and output row addresses (and the head-dim-32/64 kernel's Q copies).  Decode: every cache row a lane reads lies in the
 // split's key range inside [0, length) and inside the cache.
 //
 // --plant: compute tail-tile rows from each copy's first row (a block base) instead of
@@ -165,10 +166,37 @@ void prefill_narrow(const Prefill& p, const Rows& r, int kt, size_t kv_extent, c
     }
 }
 
+// The Q copies of the head-dim-32/64 kernel's next q-tile: wave w, lane l, k-step kc reads
+// 16 bytes at the wave's first row (clamped) plus plan::q_copy_offset, into its 1 KiB block
+// of the Q buffer.
 template <int D>
-void prefill(const Prefill& p) {
+void q_copies(const Rows& r, int q0, size_t q_extent, const std::string& ctx) {
+    constexpr int W = 4;
+    using G = NarrowGeo<D, W>;
+    for (int wave = 0; wave < W; ++wave) {
+        const int rb = imin(q0 + wave * 32, r.q_len - 1);
+        for (int lane = 0; lane < 64; ++lane) {
+            const int row = imin(q0 + wave * 32 + (lane & 31), r.q_len - 1);
+            for (int kc = 0; kc < G::KC; ++kc) {
+                const uint64_t byte = (uint64_t)(r.q_base + (size_t)rb * r.q_rs) * 2 +
+                                      q_copy_offset(row - rb, lane >> 5, r.q_rs) + 32 * kc;
+                const uint64_t want = (uint64_t)(r.q_base + (size_t)row * r.q_rs + 8 * (lane >> 5) + 16 * kc) * 2;
+                ++g_checks;
+                if (byte != want || row < 0 || row >= r.q_len || 8 * (lane >> 5) + 16 * kc + 8 > D ||
+                    byte + 16 > (uint64_t)q_extent * 2)
+                    fail(ctx + " Q copy wave " + std::to_string(wave) + " lane " + std::to_string(lane) + " kc " +
+                         std::to_string(kc) + " reads outside the q-tile's rows");
+                check_lds("Q", (long)(wave * G::KC + kc) * 1024 + 16 * lane, (long)W * G::KC * 1024, ctx);
+            }
+        }
+    }
+}
+
+template <int D>
+void prefill(const Prefill& p, int slots) {
     constexpr bool wide = D == 128;
     constexpr int BN = 64;
+    constexpr int kMaxList = 64;   // the narrow kernel's list capacity
     const int BM = wide ? WideGeo<D>::BM : NarrowGeo<D, 4>::BM;
     const Layout lay = (Layout)p.layout;
     std::vector<int> cu(p.B + 1, 0);
@@ -178,30 +206,27 @@ void prefill(const Prefill& p) {
     const size_t q_extent = lay == kUnpadded ? (size_t)tokens * p.Hq * D : (size_t)p.B * p.Hq * p.Lq * D;
     const size_t kv_extent = lay == kUnpadded ? (size_t)tokens * p.Hkv * D : (size_t)p.B * p.Hkv * p.Lk * D;
     const int n_qtiles = (p.Lq + BM - 1) / BM;
-    const long grid = (long)n_qtiles * p.Hq * p.B;
-    std::vector<char> seen((size_t)grid, 0);
+    const long tiles = (long)n_qtiles * p.Hq * p.B;
+    std::vector<char> seen((size_t)tiles, 0);
     const int qgrp = p.Hq / p.Hkv;
-    for (long blk = 0; blk < grid; ++blk) {
-        const BlockCoord bc = map_block((unsigned)blk, n_qtiles, p.B, p.Hq, p.Hkv,
-                                        p.causal != 0 || !p.lens.empty() || lay == kUnpadded, 8);
+
+    // one (q-tile, item, head): its rows, Q / output addresses, key tiles and their copies
+    auto tile = [&](int qt, int b, int h, const std::string& ctx) {
         ++g_checks;
-        if (bc.qt < 0 || bc.qt >= n_qtiles || bc.b < 0 || bc.b >= p.B || bc.h < 0 || bc.h >= p.Hq) {
-            fail("block " + std::to_string(blk) + " maps outside the grid");
-            continue;
+        if (qt < 0 || qt >= n_qtiles || b < 0 || b >= p.B || h < 0 || h >= p.Hq) {
+            fail(ctx + " maps outside the grid");
+            return;
         }
-        char& s = seen[((size_t)bc.qt * p.B + bc.b) * p.Hq + bc.h];
-        if (s) fail("block " + std::to_string(blk) + " maps onto a (q-tile, item, head) already taken");
+        char& s = seen[((size_t)qt * p.B + b) * p.Hq + h];
+        if (s) fail(ctx + " maps onto a (q-tile, item, head) already taken");
         s = 1;
-        const int kvh = bc.h / qgrp;
+        const int kvh = h / qgrp;
         const bool has_len = lay != kUnpadded && !p.lens.empty();
-        const Rows r = item_rows(lay, bc.b, bc.h, kvh, D, p.Hq, p.Hkv, p.Lq, p.Lk, cu[bc.b],
-                                 lay == kUnpadded ? cu[bc.b + 1] : 0, has_len, has_len ? p.lens[bc.b] : 0);
-        const int q0 = bc.qt * BM;
-        if (q0 >= r.q_len) continue;
+        const Rows r = item_rows(lay, b, h, kvh, D, p.Hq, p.Hkv, p.Lq, p.Lk, cu[b], lay == kUnpadded ? cu[b + 1] : 0,
+                                 has_len, has_len ? p.lens[b] : 0);
+        const int q0 = qt * BM;
+        if (q0 >= r.q_len) return;
         const int last_row = imin(q0 + BM, r.q_len) - 1;
-        const std::string ctx = "prefill D" + std::to_string(D) + " block " + std::to_string(blk) + " (qt " +
-                                std::to_string(bc.qt) + ", b " + std::to_string(bc.b) + ", h " +
-                                std::to_string(bc.h) + ")";
         // Q rows the workgroup loads (clamped to the last row) and the rows it stores
         for (int row = q0; row < q0 + BM; ++row) {
             const size_t at = r.q_base + (size_t)imin(row, r.q_len - 1) * r.q_rs;
@@ -210,6 +235,7 @@ void prefill(const Prefill& p) {
             if (row < r.q_len && r.q_base + (size_t)row * r.q_rs + D > q_extent)
                 fail(ctx + " output row " + std::to_string(row) + " outside out");
         }
+        if (!wide) q_copies<D>(r, q0, q_extent, ctx);
         const Tiles t = key_tiles(span_union(p.P + q0, p.P + last_row, r.kv_valid, p.causal != 0, p.W), BN);
         for (int kt = t.begin; kt < t.end; ++kt) {
             ++g_checks;
@@ -219,10 +245,91 @@ void prefill(const Prefill& p) {
             else
                 prefill_narrow<D>(p, r, kt, kv_extent, ctx);
         }
+    };
+
+    if (wide) {
+        for (long blk = 0; blk < tiles; ++blk) {
+            const BlockCoord bc = map_block((unsigned)blk, n_qtiles, p.B, p.Hq, p.Hkv,
+                                            p.causal != 0 || !p.lens.empty() || lay == kUnpadded, 8);
+            tile(bc.qt, bc.b, bc.h,
+                 "prefill D" + std::to_string(D) + " block " + std::to_string(blk) + " (qt " + std::to_string(bc.qt) +
+                     ", b " + std::to_string(bc.b) + ", h " + std::to_string(bc.h) + ")");
+        }
+    } else {
+        // the persistent grid: every workgroup's list, at most kMaxList q-tiles long; with
+        // per-item lengths for at most kRankedItems items the lists follow the ranked order
+        const bool ranked = !p.lens.empty() && p.B <= kRankedItems;
+        std::vector<int> order(p.B), ne(p.B), nrow(p.B), cost(p.B);
+        std::vector<long> start_ne(p.B), start_z(p.B);
+        long n_ne = 0, n_z = 0;
+        if (ranked) {
+            for (int b = 0; b < p.B; ++b) {
+                const int rows = lay == kUnpadded ? imin(imax(p.lens[b], 0), p.Lq) : p.Lq;
+                const int valid = lay == kUnpadded ? rows : imin(imax(p.lens[b], 0), p.Lk);
+                const ItemSched is = item_sched(rows, valid, p.P, p.causal != 0, p.W, BM, BN);
+                ne[b] = is.ne;
+                nrow[b] = is.nrow;
+                cost[b] = is.cost;
+            }
+            for (int b = 0; b < p.B; ++b) {
+                int rank = 0;
+                for (int x = 0; x < p.B; ++x) rank += ranks_before(cost[x], x, cost[b], b) ? 1 : 0;
+                order[rank] = b;
+            }
+            for (int r = 0; r < p.B; ++r) {
+                start_ne[r] = n_ne;
+                n_ne += (long)ne[order[r]] * p.Hq;
+            }
+            for (int b = 0; b < p.B; ++b) {
+                start_z[b] = n_z;
+                n_z += (long)(nrow[b] - ne[b]) * p.Hq;
+                // q-tiles without rows are in no list
+                for (int qt = nrow[b]; qt < n_qtiles; ++qt)
+                    for (int h = 0; h < p.Hq; ++h) seen[((size_t)qt * p.B + b) * p.Hq + h] = 1;
+            }
+        }
+        const int wgs = persist_grid(tiles, slots, 8, kMaxList);
+        ++g_checks;
+        if (wgs % 8 != 0 || wgs <= 0) fail("prefill D" + std::to_string(D) + " grid of " + std::to_string(wgs));
+        for (int wg = 0; wg < wgs; ++wg) {
+            ++g_checks;
+            if (persist_pos(wg, kMaxList, wgs, 8) < tiles)
+                fail("prefill D" + std::to_string(D) + " workgroup " + std::to_string(wg) + " of " +
+                     std::to_string(wgs) + " has more than " + std::to_string(kMaxList) + " q-tiles");
+            for (int k = 0; k < kMaxList; ++k) {
+                const long pos = persist_pos(wg, k, wgs, 8);
+                TileRef tr{};
+                if (ranked) {
+                    const RankedRef rr = ranked_tile(pos, p.B, p.Hq, n_ne, n_z, order.data(), start_ne.data(),
+                                                     start_z.data(), ne.data(), nrow.data());
+                    if (rr.kind == 2) break;
+                    tr = {rr.b, rr.h, rr.qt};
+                    // the kind the kernel derives from the q-tile's key tiles must agree
+                    const int rows = lay == kUnpadded ? imin(imax(p.lens[rr.b], 0), p.Lq) : p.Lq;
+                    const int valid = lay == kUnpadded ? rows : imin(imax(p.lens[rr.b], 0), p.Lk);
+                    const int q0 = rr.qt * BM;
+                    ++g_checks;
+                    if (q0 >= rows) {
+                        fail("ranked q-tile without rows");
+                    } else {
+                        const Tiles t = key_tiles(
+                            span_union(p.P + q0, p.P + imin(q0 + BM, rows) - 1, valid, p.causal != 0, p.W), BN);
+                        if ((t.end > t.begin) != (rr.kind == 0)) fail("ranked q-tile of the wrong kind");
+                    }
+                } else {
+                    if (pos >= tiles) break;
+                    tr = persist_tile(pos, p.Hq, n_qtiles);
+                }
+                tile(tr.qt, tr.b, tr.h,
+                     "prefill D" + std::to_string(D) + " workgroup " + std::to_string(wg) + " of " +
+                         std::to_string(wgs) + " entry " + std::to_string(k) + " (qt " + std::to_string(tr.qt) +
+                         ", b " + std::to_string(tr.b) + ", h " + std::to_string(tr.h) + ")");
+            }
+        }
     }
-    for (long i = 0; i < grid; ++i)
+    for (long i = 0; i < tiles; ++i)
         if (!seen[(size_t)i]) {
-            fail("(q-tile, item, head) " + std::to_string(i) + " has no block");
+            fail("(q-tile, item, head) " + std::to_string(i) + " has no workgroup");
             break;
         }
 }
@@ -283,12 +390,18 @@ int main(int argc, char** argv) {
                 std::printf("FAIL unreadable line: %s\n", line.c_str());
                 return 2;
             }
-            if (p.D == 32)
-                prefill<32>(p);
-            else if (p.D == 64)
-                prefill<64>(p);
-            else if (p.D == 128)
-                prefill<128>(p);
+            // the narrow kernel's grid depends on the device's workgroup slots: MI355X's
+            // 512, and small counts whose lists run long
+            if (p.D == 32 || p.D == 64) {
+                for (int slots : {512, 40, 8}) {
+                    if (p.D == 32)
+                        prefill<32>(p, slots);
+                    else
+                        prefill<64>(p, slots);
+                }
+            } else if (p.D == 128) {
+                prefill<128>(p, 0);
+            }
         } else if (kind == "decode") {
             int mode, B, Hq, Hkv, cap, kv_len, D, P, W, n;
             in >> mode >> B >> Hq >> Hkv >> cap >> kv_len >> D >> P >> W >> n;
