@@ -126,17 +126,23 @@ def test_long_prefill_sampled_rows(mi, ref):
 
 
 def test_many_items(mi, ref):
-    """16384 items of 4 heads: 65536 workgroups, the one-dimensional grid's block index
-    past 2^16; padded lengths; sampled items against the oracle."""
+    """16384 items of 4 heads: 65536 q-tiles, so the head-dim-64 kernel's persistent grid
+    grows past the resident workgroups to keep every list within 64 q-tiles; padded
+    lengths.  The output starts as NaN: every element must be written (rows past an
+    item's length as zeros); sampled items against the oracle."""
     import torch
     B, Hq, Hkv, L, D = 16384, 4, 1, 64, 64
     say("many items: 16384")
     x = W.random_prefill(53, B, Hq, Hkv, L, L, D, "bf16", seq_len_range=(1, 64))
     scale = 1.0 / math.sqrt(D)
-    got = mi.attn_prefill(to_gpu(x["q"]), to_gpu(x["k"]), to_gpu(x["v"]), seq_lens=to_gpu(x["seq_lens"]),
-                          scale=scale)
+    out = torch.full((B, Hq, L, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mi.attn_prefill(to_gpu(x["q"]), to_gpu(x["k"]), to_gpu(x["v"]), out, seq_lens=to_gpu(x["seq_lens"]),
+                    scale=scale)
     torch.cuda.synchronize()
-    g = to_f64(got)
+    g = to_f64(out)
+    assert np.all(np.isfinite(g)), "a q-tile of the output was not written"
+    lens = x["seq_lens"]
+    assert all(np.all(g[b, :, int(lens[b]):] == 0.0) for b in range(0, B, 97)), "padded rows must be zero"
     for b in (0, 1, 8191, 16382, 16383):
         want = ref.prefill(x["q"][b:b + 1], x["k"][b:b + 1], x["v"][b:b + 1], scale=scale,
                            seq_lens=x["seq_lens"][b:b + 1])

@@ -78,9 +78,10 @@ PREFILL_CASES = [
     (2, 4, 4, 333, 333, 64, False, 0, None, 128, "f16"),
     (3, 6, 3, 200, 200, 32, False, 0, [200, 1, 0], 0, "f16"),
     (2, 2, 2, 100, 150, 64, True, 50, [150, 120], 0, "f16"),
-    # head dims 32/64 with a narrow band (the banded kernel): several tiles per segment,
-    # GQA and a padded item; a causal window; a position offset with fp16; a causal
-    # window one key wider than the bidirectional one; a band too wide for its ring
+    # head dims 32/64 with narrow bands over long sequences (many q-tiles per workgroup
+    # list of the persistent grid): GQA and a padded item; a causal window; a position
+    # offset with fp16; a causal window one key wider than the bidirectional one; a band
+    # wider than a q-tile
     (2, 6, 2, 9000, 9000, 64, False, 0, [9000, 8100], 128, "bf16"),
     (1, 4, 4, 5000, 5000, 32, True, 0, None, 96, "bf16"),
     (1, 8, 8, 3000, 3100, 64, False, 100, None, 64, "f16"),

@@ -62,7 +62,7 @@ VARLEN_CASES = [
     ([100, 33, 0, 7], 4, 4, 32, True, 16, "f32"),
     ([300, 0, 17, 513], 4, 4, 64, False, 0, "f16"),
     ([257, 1, 300], 8, 2, 128, True, 0, "f16"),
-    # the banded kernel over unpadded items (bidirectional and causal windows)
+    # narrow bands over unpadded items at head dims 32/64 (bidirectional and causal windows)
     ([1000, 5, 700, 129], 4, 2, 64, False, 128, "bf16"),
     ([900, 33], 2, 2, 32, True, 64, "f16"),
 ]
