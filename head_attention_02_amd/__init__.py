@@ -18,6 +18,8 @@ missing library or GPU raises.
                           scale=None, workspace=None)
     attn_decode_append(q, k_new, v_new, k_caches, v_caches, cache_lens, out=None, *,
                        window=0, scale=None, workspace=None)
+    attn_decode_append_qkv(qkv, k_caches, v_caches, cache_lens, out=None, *, window=0,
+                           scale=None, workspace=None)
     attn_decode_noalloc(q, k_cache, v_cache, out=None, *, kv_len=None, pos_offset=None,
                         kv_lens=None, window=0, scale=None)
     attn_decode_workspace_bytes(batch, q_heads, kv_heads, kv_len, head_dim)
@@ -42,8 +44,8 @@ MI_ATTN_F32, MI_ATTN_BF16, MI_ATTN_F16 = 0, 1, 2
 MI_ATTN_OK, MI_ATTN_ERR_INVALID, MI_ATTN_ERR_UNSUPPORTED, MI_ATTN_ERR_HIP = 0, 1, 2, 3
 
 EXPORTS = ("attn_prefill", "attn_prefill_token_major", "attn_prefill_varlen", "attn_decode", "attn_decode_noalloc",
-           "attn_decode_per_cache", "attn_decode_append", "attn_decode_workspace_bytes", "attn_last_error",
-           "attn_version")
+           "attn_decode_per_cache", "attn_decode_append", "attn_decode_append_qkv", "attn_decode_workspace_bytes",
+           "attn_last_error", "attn_version")
 
 
 class MiAttnError(RuntimeError):
@@ -77,6 +79,8 @@ def library() -> ctypes.CDLL:
         lib.attn_decode_per_cache.restype = i
         lib.attn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, i, f, i, vp, sz, vp]
         lib.attn_decode_append.restype = i
+        lib.attn_decode_append_qkv.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, i, f, i, vp, sz, vp]
+        lib.attn_decode_append_qkv.restype = i
         lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
         lib.attn_decode_workspace_bytes.restype = sz
         lib.attn_last_error.argtypes = []
@@ -401,6 +405,33 @@ def attn_decode_append(q, k_new, v_new, k_caches, v_caches, cache_lens, out=None
                                       _dev(kp, "k_caches"), _dev(vp, "v_caches"), _dev(out, "out"), B, Hq, Hkv,
                                       cap, D, _dev(cache_lens, "cache_lens"), window, float(scale), dt,
                                       _dev(workspace, "workspace"), ws_bytes, _stream(stream))
+    _keep_for(stream, kp, vp)
+    _check(st)
+    return out
+
+
+def attn_decode_append_qkv(qkv, k_caches, v_caches, cache_lens, out=None, *, window: int = 0,
+                           scale: float | None = None, workspace=None, stream=None):
+    """attn_decode_append with the new token's query, key and value read from one fused row
+    per item: qkv [batch, q_heads + 2 * kv_heads, head_dim], contiguous (the query heads,
+    then the key heads, then the value heads); returns `out` [batch, q_heads, head_dim]."""
+    dt = _dtype_code(qkv)
+    if qkv.dim() != 3 or not qkv.is_contiguous():
+        raise ValueError("qkv must be a contiguous [batch, q_heads + 2 * kv_heads, head_dim] tensor")
+    _, (Hkv, _, _) = _cache_pointers(k_caches, qkv.shape[0], "k_caches", qkv.dtype, qkv.device)
+    Hq = qkv.shape[1] - 2 * Hkv
+    if Hq < 1:
+        raise ValueError("qkv holds no query head beside the 2 * kv_heads key and value rows")
+    if out is None:
+        out = _torch().empty((qkv.shape[0], Hq, qkv.shape[2]), dtype=qkv.dtype, device=qkv.device)
+    B, Hq, Hkv, cap, D, kp, vp, out, workspace, ws_bytes = _decode_common(qkv[:, :Hq], k_caches, v_caches,
+                                                                          cache_lens, out, workspace, "cache_lens")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = library().attn_decode_append_qkv(_dev(qkv, "qkv"), _dev(kp, "k_caches"), _dev(vp, "v_caches"),
+                                          _dev(out, "out"), B, Hq, Hkv, cap, D, _dev(cache_lens, "cache_lens"),
+                                          window, float(scale), dt, _dev(workspace, "workspace"), ws_bytes,
+                                          _stream(stream))
     _keep_for(stream, kp, vp)
     _check(st)
     return out

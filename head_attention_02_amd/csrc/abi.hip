@@ -278,6 +278,8 @@ int decode_stacked(const char* fn, const void* q, const void* k_cache, const voi
     a.splits = p.splits;
     a.split_len = p.split_len;
     a.head_groups = p.head_groups;
+    a.q_rs = q_heads * head_dim;
+    a.new_rs = kv_heads * head_dim;
     hipError_t e = mi_attn::launch_decode(a, head_dim, p.heads_per_group, dtype,
                                           (hipStream_t)stream);
     if (e != hipSuccess) return fail(MI_ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
@@ -310,10 +312,12 @@ int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
 namespace {
 
 // Shared checks and launch of the per-item-cache decode calls.
+// fused_rs > 0: q, k_new and v_new are the parts of one fused row per item of fused_rs
+// elements (attn_decode_append_qkv); 0: the separate [batch, heads, head_dim] tensors.
 int decode_per_item(const char* fn, const void* q, const void* const* k_caches, const void* const* v_caches,
                     const void* k_new, const void* v_new, void* out, int batch, int q_heads, int kv_heads,
                     int capacity, int head_dim, const int32_t* lens, int window, float scale, int dtype,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+                    void* workspace, size_t workspace_bytes, void* stream, int fused_rs = 0) {
     g_error[0] = '\0';
     if (dtype != MI_ATTN_BF16 && dtype != MI_ATTN_F32 && dtype != MI_ATTN_F16)
         return fail(MI_ATTN_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
@@ -366,6 +370,8 @@ int decode_per_item(const char* fn, const void* q, const void* const* k_caches, 
     a.splits = p.splits;
     a.split_len = p.split_len;
     a.head_groups = p.head_groups;
+    a.q_rs = fused_rs > 0 ? fused_rs : q_heads * head_dim;
+    a.new_rs = fused_rs > 0 ? fused_rs : kv_heads * head_dim;
     hipError_t e = mi_attn::launch_decode(a, head_dim, p.heads_per_group, dtype,
                                           (hipStream_t)stream);
     if (e != hipSuccess) return fail(MI_ATTN_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
@@ -396,6 +402,26 @@ int attn_decode_append(const void* q, const void* k_new, const void* v_new, void
     return decode_per_item("attn_decode_append", q, (const void* const*)k_caches, (const void* const*)v_caches,
                            k_new, v_new, out, batch, q_heads, kv_heads, capacity, head_dim, cache_lens, window,
                            scale, dtype, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_append_qkv(const void* qkv, void* const* k_caches, void* const* v_caches, void* out, int batch,
+                           int q_heads, int kv_heads, int capacity, int head_dim, const int32_t* cache_lens,
+                           int window, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    g_error[0] = '\0';
+    if (batch > 0 && !qkv) return fail(MI_ATTN_ERR_INVALID, "attn_decode_append_qkv: null fused row");
+    if (q_heads < 1 || kv_heads < 1 || head_dim < 1 ||
+        (long)(q_heads + 2L * kv_heads) * head_dim > 0x7fffffffL)
+        return fail(MI_ATTN_ERR_INVALID, "attn_decode_append_qkv: bad head counts (%d, %d) or head_dim %d",
+                    q_heads, kv_heads, head_dim);
+    const size_t esize = dtype == MI_ATTN_F32 ? 4 : 2;
+    const char* row = (const char*)qkv;
+    const void* k_new = qkv ? row + (size_t)q_heads * head_dim * esize : nullptr;
+    const void* v_new = qkv ? row + (size_t)(q_heads + kv_heads) * head_dim * esize : nullptr;
+    return decode_per_item("attn_decode_append_qkv", qkv, (const void* const*)k_caches,
+                           (const void* const*)v_caches, k_new, v_new, out, batch, q_heads, kv_heads, capacity,
+                           head_dim, cache_lens, window, scale, dtype, workspace, workspace_bytes, stream,
+                           (q_heads + 2 * kv_heads) * head_dim);
 }
 
 }  // extern "C"

@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     u32x4 qw[GT][NW];
 #pragma unroll
     for (int t = 0; t < GT; ++t) {
-        const size_t q_at = ((size_t)b * a.q_heads + h0 + t) * D + 8 * c;
+        const size_t q_at = (size_t)b * a.q_rs + (size_t)(h0 + t) * D + 8 * c;
         if constexpr (PACKED) {
 #pragma unroll
             for (int w = 0; w < NW; ++w) qw[t][w] = *(const u32x4*)((const uint16_t*)a.q + q_at + w * (D / NW));
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     // lanes that read it), not from the cache; the split that holds the position also
     // stores the new rows into the cache (first head group only).  No other workgroup
     // reads that slot, so the store does not race with the reads.
-    const size_t new_row = ((size_t)b * a.kv_heads + kvh) * D + 8 * c;
+    const size_t new_row = (size_t)b * a.new_rs + (size_t)kvh * D + 8 * c;
     if constexpr (MODE == kAppend) {
         if (hg == 0 && pos >= s0 && pos < s1 && tid < LPR) {
 #pragma unroll

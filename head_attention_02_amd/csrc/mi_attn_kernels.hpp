@@ -71,6 +71,10 @@ struct DecodeArgs {
     // holds the cache lengths before the append.  nullptr: no append.
     const void* k_new;
     const void* v_new;
+    // Elements from one item's queries to the next item's (q_heads * head_dim, or the
+    // fused QKV row's length for attn_decode_append_qkv), and from one item's new K/V
+    // rows to the next item's (kv_heads * head_dim, or the fused row's length).
+    int q_rs, new_rs;
 };
 
 // Each launcher enqueues on `stream` and returns the launch status.

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MI_ATTN_VERSION 6
+#define MI_ATTN_VERSION 7
 
 typedef enum { MI_ATTN_F32 = 0, MI_ATTN_BF16 = 1, MI_ATTN_F16 = 2 } mi_attn_dtype;
 
@@ -245,6 +245,28 @@ int attn_decode_append(const void* q, const void* k_new, const void* v_new, void
                        void* const* v_caches, void* out, int batch, int q_heads, int kv_heads, int capacity,
                        int head_dim, const int32_t* cache_lens, int window, float scale, int dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_append_qkv -- attn_decode_append reading the new token's query, key and
+ * value from one fused row per item, as a fused QKV projection writes it.  The row layout
+ * is that of `split_qkv` on the ferrum-kernels `Backend` page (Required Methods): per
+ * token [q_dim + 2 * kv_dim] with q_dim = q_heads * head_dim and kv_dim = kv_heads *
+ * head_dim, the query heads first, then the key heads, then the value heads;
+ * `split_qkv_norm_rope_into_cache` (Provided Methods) on the same page consumes such a
+ * row and writes its K/V straight into the cache.  Here the row's parts enter as given:
+ * a caller that normalises or rotates q and k does so before the call.
+ *
+ *   qkv         [batch, q_heads + 2 * kv_heads, head_dim], 16-byte aligned: item b's row
+ *               holds its q heads, then its kv_heads key rows, then its kv_heads value rows
+ *   k_caches, v_caches, out, batch, q_heads, kv_heads, capacity, head_dim, cache_lens,
+ *   window, scale, dtype, workspace: as for attn_decode_append (the workspace query is the
+ *   same).  Errors as for attn_decode_append; a null qkv with batch > 0 is
+ *   MI_ATTN_ERR_INVALID.
+ */
+int attn_decode_append_qkv(const void* qkv, void* const* k_caches, void* const* v_caches, void* out, int batch,
+                           int q_heads, int kv_heads, int capacity, int head_dim, const int32_t* cache_lens,
+                           int window, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /* Scratch bytes attn_decode needs for these sizes (0 when it needs none): the split
  * decode's partial states [batch, q_heads, splits, head_dim + 2] fp32 when the launch plan

@@ -206,9 +206,30 @@ def test_decode_append_validation(kw, status, msg):
     assert err.startswith("attn_decode_append: ") and msg in err
 
 
+def append_qkv(**kw):
+    args = dict(qkv=FAKE, kc=FAKE, vc=FAKE, out=FAKE, batch=2, q_heads=8, kv_heads=2, capacity=16, head_dim=64,
+                cache_lens=FAKE, window=0, scale=0.125, dtype=mi.MI_ATTN_BF16, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return mi.library().attn_decode_append_qkv(*args.values())
+
+
+@pytest.mark.parametrize("kw,status,msg", [e for e in COMMON_PER_ITEM_ERRORS if "q_heads" not in e[0]] + [
+    (dict(cache_lens=None), mi.MI_ATTN_ERR_INVALID, "null"),
+    (dict(qkv=None), mi.MI_ATTN_ERR_INVALID, "null fused row"),
+    (dict(qkv=ctypes.c_void_p(0x100004)), mi.MI_ATTN_ERR_INVALID, "aligned"),
+    (dict(q_heads=0), mi.MI_ATTN_ERR_INVALID, "head counts"),
+    (dict(q_heads=6, kv_heads=4), mi.MI_ATTN_ERR_INVALID, "not a multiple"),
+])
+def test_decode_append_qkv_validation(kw, status, msg):
+    assert append_qkv(**kw) == status
+    err = mi.attn_last_error()
+    assert err.startswith("attn_decode_append_qkv: ") and msg in err
+
+
 def test_per_item_empty_batch_is_ok_without_a_gpu():
     assert per_cache(batch=0, kv_lens=None) == mi.MI_ATTN_OK
     assert append(batch=0, k_new=None, v_new=None) == mi.MI_ATTN_OK
+    assert append_qkv(batch=0, qkv=None) == mi.MI_ATTN_OK
 
 
 def varlen(**kw):

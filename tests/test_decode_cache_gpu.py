@@ -200,3 +200,36 @@ def test_named_decode_append_workload(mi, ref):
     record(w.name, check(to_f64(got), want, w.dtype, w.name))
     assert np.array_equal(_host(kd, w.dtype), np.stack(k_after)), "K caches after the append"
     assert np.array_equal(_host(vd, w.dtype), np.stack(v_after)), "V caches after the append"
+
+
+QKV_CASES = [
+    # B, Hq, Hkv, capacity, D, cache lengths (before the append), window, dtype
+    (4, 32, 8, 1024, 128, [999, 0, 1023, 1024], 0, "bf16"),
+    (3, 12, 4, 513, 64, [512, 99, 2], 64, "f16"),
+    (3, 6, 2, 256, 32, [199, 49, 255], 0, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", QKV_CASES, ids=_ids)
+def test_decode_append_qkv(mi, ref, case):
+    """The new token's q, k and v read from one fused row per item [q heads | k heads | v
+    heads] (ferrum-kernels `Backend` page, `split_qkv` layout): against the oracle on the
+    split tensors, and bit for bit against attn_decode_append on them (outputs and caches)."""
+    import torch
+    B, Hq, Hkv, cap, D, lens, Wn, dt = case
+    say(f"decode_append_qkv case {case}")
+    q, kc, vc, kn, vn = _items(26, B, Hq, Hkv, cap, D, dt)
+    lens = np.array(lens, np.int32)
+    qkv = np.concatenate([q, kn, vn], axis=1)   # [B, Hq + 2 Hkv, D]
+    scale = 1.0 / math.sqrt(D)
+    want, k_after, v_after = ref.decode_append(q, kn, vn, kc, vc, lens, scale=scale, window=Wn)
+    kd, vd = [to_gpu(c) for c in kc], [to_gpu(c) for c in vc]
+    got = mi.attn_decode_append_qkv(to_gpu(qkv), kd, vd, to_gpu(lens), window=Wn, scale=scale)
+    kd2, vd2 = [to_gpu(c) for c in kc], [to_gpu(c) for c in vc]
+    split = mi.attn_decode_append(to_gpu(q), to_gpu(kn), to_gpu(vn), kd2, vd2, to_gpu(lens), window=Wn, scale=scale)
+    torch.cuda.synchronize()
+    record(f"decode_append_qkv {case[:5]}", check(to_f64(got), want, dt, f"decode_append_qkv {case}"))
+    assert torch.equal(got, split), "fused-row and split calls must agree bit for bit"
+    for b in range(B):
+        assert np.array_equal(_bits(_host(kd[b], dt)), _bits(k_after[b])), f"K cache of item {b} after the append"
+        assert np.array_equal(_bits(_host(vd[b], dt)), _bits(v_after[b])), f"V cache of item {b} after the append"
