@@ -451,13 +451,16 @@ def kernel_sources(w: W.Workload):
     return ["prefill_bf16_narrow.hip", "mi_attn_device.hpp", "mi_attn_kernels.hpp"]
 
 
-def kernel_entry(w: W.Workload, x: dict, times_ms) -> dict:
-    """One workload's figures from its per-launch times: the mean launch time, the rate of
-    algorithmic work, and the roofline fraction -- the larger of the two floors (FLOPs at
-    the MFMA peak, bytes at the HBM peak) over the measured time; `bound` names the floor
-    that is larger.  A workload below a microsecond of floor is latency-bound: its
-    fraction is given, but the time is what counts."""
-    ms = float(np.mean(times_ms))
+def kernel_entry(w: W.Workload, x: dict, mean_ms: float, times_ms) -> dict:
+    """One workload's figures: mean_ms, the mean launch time of K launches back to back (one
+    event pair around them), gives the rate of algorithmic work and the roofline fraction
+    -- the larger of the two floors (FLOPs at the MFMA peak, bytes at the HBM peak) over
+    the measured time; `bound` names the floor that is larger.  times_ms, the launches of a
+    second pass timed one by one (an event between every two, which adds a few
+    microseconds to each), give the median and the minimum.  A workload below a
+    microsecond of floor is latency-bound: its fraction is given, but the time is what
+    counts."""
+    ms = float(mean_ms)
     sec = ms / 1e3
     src = kernel_sources(w)
     if w.kind in ("decode", "decode_append"):
@@ -477,8 +480,8 @@ def kernel_entry(w: W.Workload, x: dict, times_ms) -> dict:
         achieved, peak, unit = fl / sec / 1e12, peak_f, "TFLOP/s"
     e = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": floor / sec,
          "traffic": traffic_from_profiles(w.name, kernel_sources_digest(src)),
-         "kernel_us": ms * 1e3, "kernel_us_median": float(np.median(times_ms)) * 1e3,
-         "kernel_us_min": float(np.min(times_ms)) * 1e3,
+         "kernel_us": ms * 1e3, "kernel_us_median_single": float(np.median(times_ms)) * 1e3,
+         "kernel_us_min_single": float(np.min(times_ms)) * 1e3,
          "TFLOPs": fl / sec / 1e12, "frac_of_mfma_peak": fl / sec / 1e12 / peak_f,
          "GBps": by / sec / 1e9, "frac_of_hbm_peak": by / sec / 1e9 / PEAK_HBM_GBPS,
          "algorithmic_flop": fl, "algorithmic_bytes": by,
@@ -539,14 +542,16 @@ def main() -> int:
         runners.append(Runner(w, x))
     torch.cuda.synchronize()
 
-    # Each workload in turn: W warm-up launches, then K timed launches back to back with an
-    # event between every two, so that a workload is timed in the clock and cache state
-    # its own launches leave (the chip's clock follows the power of the last milliseconds
-    # of work: a causal prefill launched right after milliseconds of HBM-bound decode ran
-    # its first launches 20 % slower).  The K launches of all workloads are the K steps of
-    # the timed region.
+    # Each workload in turn: W warm-up launches, then K timed launches back to back with one
+    # event before and one after them, so that a workload is timed in the clock and cache
+    # state its own launches leave (the chip's clock follows the power of the last
+    # milliseconds of work: a causal prefill launched right after milliseconds of HBM-bound
+    # decode ran its first launches 20 % slower).  The K launches of all workloads are the K
+    # steps of the timed region.  A second pass, after the timed region, times K launches of
+    # each workload one by one for the spread (an event between every two launches adds a
+    # few microseconds to each, so the mean comes from the first pass).
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(K + 1)] for _ in runners]
+    spans = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in runners]
     begin, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -555,21 +560,32 @@ def main() -> int:
         for _ in range(args.warmup):
             r()
         torch.cuda._sleep(1_000_000)   # keep the queue ahead of the GPU so events time kernels, not launches
+        spans[i][0].record()
+        for s in range(K):
+            r()
+        spans[i][1].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean_ms = [a.elapsed_time(b) / K for a, b in spans]
+    step_ms = sum(mean_ms)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(K + 1)] for _ in runners]
+    for i, r in enumerate(runners):
+        for _ in range(args.warmup):
+            r()
+        torch.cuda._sleep(1_000_000)
         ev[i][0].record()
         for s in range(K):
             r()
             ev[i][s + 1].record()
-    end.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per_launch = [[ev[i][s].elapsed_time(ev[i][s + 1]) for s in range(K)] for i in range(len(runners))]
-    step_ms = sum(ev[i][0].elapsed_time(ev[i][K]) for i in range(len(runners))) / K
 
     result = {"metric": "attention TFLOP/s (prefill, % MFMA peak); decode KV GB/s (% HBM peak)",
               "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": step_ms,
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
               "data": "synthetic (seeded N(0, sigma^2), bf16 by round-to-nearest-even)"}
-    rooflines = {w.name: kernel_entry(w, x, t) for w, x, t in zip(ws, inputs, per_launch)}
+    rooflines = {w.name: kernel_entry(w, x, m, t) for w, x, m, t in zip(ws, inputs, mean_ms, per_launch)}
     head = ws[0] if args.workload != "headline" else W.WORKLOADS[HEADLINE_VALUE]
     r0 = rooflines[head.name]
     result["value"] = r0["achieved"]
