@@ -92,8 +92,7 @@ struct Prefill {
     uint32_t k_cb[G::NKW];      // byte offset of this wave's K copy ii from the tile base (uniform)
     uint32_t v_cb[G::NVW];      // ... V
     int lo_r, hi_r;             // this lane's key interval
-    bool all_rows_valid;
-    int inter_lo, inter_hi;     // keys every row of the wave sees
+    int inter_lo, inter_hi;     // keys every row of the wave that sees a key sees
     int union_lo, union_hi;     // keys some row of the wave sees (a superset; empty if hi < lo)
     float c2;                   // scale * log2(e)
 
@@ -237,7 +236,7 @@ struct Prefill {
             return;
         }
         const int kbase = kt * kBN;
-        const bool full = FULL || (all_rows_valid && kbase >= inter_lo && kbase + kBN - 1 <= inter_hi);
+        const bool full = FULL || (kbase >= inter_lo && kbase + kBN - 1 <= inter_hi);
         if (!full) {
             keep_branch();
             // key jj is kept iff lo <= jj <= hi, tested as one unsigned compare
@@ -369,7 +368,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
         st.inter_hi = k.inter.hi;
         st.union_lo = k.uni.lo;
         st.union_hi = k.uni.hi;
-        st.all_rows_valid = k.all_rows_valid;
     }
 
     // ---- Q^T operand: lane l holds row l%32, dims 16*kc + 8*g + [0, 8) ---------------
@@ -485,7 +483,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
     // ---- epilogue: normalise, zero padded / empty rows, store in the input format -----
     const float l_tot = halves_sum(st.l_run);
     if (my_row >= q_len) return;
-    const float inv = (st.hi_r >= 0 && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
+    // a row that sees no key is written as zeros by a select, whatever its (unmasked) sums
+    const bool keep = st.hi_r >= 0 && l_tot > 0.0f;
+    const float inv = keep ? 1.0f / l_tot : 0.0f;
     uint16_t* orow = (uint16_t*)a.out + ir.q_base + (size_t)my_row * ir.q_rs;
 #pragma unroll
     for (int db = 0; db < G::DB; ++db) {
@@ -493,8 +493,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
         for (int e4 = 0; e4 < 4; ++e4) {
             const int d = 32 * db + 8 * e4 + 4 * g;
             u32x2 w;
-            w[0] = H::pack2(st.o[db][4 * e4] * inv, st.o[db][4 * e4 + 1] * inv);
-            w[1] = H::pack2(st.o[db][4 * e4 + 2] * inv, st.o[db][4 * e4 + 3] * inv);
+            w[0] = H::pack2(keep ? st.o[db][4 * e4] * inv : 0.0f, keep ? st.o[db][4 * e4 + 1] * inv : 0.0f);
+            w[1] = H::pack2(keep ? st.o[db][4 * e4 + 2] * inv : 0.0f, keep ? st.o[db][4 * e4 + 3] * inv : 0.0f);
             *(u32x2*)(orow + d) = w;
         }
     }

@@ -65,8 +65,7 @@ struct Prefill {
     int v_read[G::DB];          // LDS byte offsets of this lane's transposing V reads
     // the q-tile whose scores the next Q.K^T produces (its mask)
     int lo_r[RB], hi_r[RB];     // this lane's key interval, per row block
-    bool blk_all_rows_valid[RB];
-    int b_inter_lo[RB], b_inter_hi[RB];  // keys every row of a row block sees
+    int b_inter_lo[RB], b_inter_hi[RB];  // keys every row of a row block that sees a key sees
     float c2;                   // scale * log2(e)
 
     // ---- running state ----------------------------------------------------------------
@@ -245,7 +244,7 @@ struct Prefill {
         const int kbase = kt * kBN;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            const bool full = blk_all_rows_valid[rb] && kbase >= b_inter_lo[rb] && kbase + kBN - 1 <= b_inter_hi[rb];
+            const bool full = kbase >= b_inter_lo[rb] && kbase + kBN - 1 <= b_inter_hi[rb];
             if (!full) {
                 keep_branch();
                 // key jj is kept iff lo <= jj <= hi, tested as one unsigned compare
@@ -370,15 +369,18 @@ __device__ __forceinline__ unsigned long long uni64(unsigned long long x) {
 }
 
 // Exclusive prefix sum of x over the 64 lanes of the wave; total: the sum over all.
-__device__ __forceinline__ long wave_excl_scan(long x, int lane, long& total) {
-    long inc = x;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const long y = __shfl_up(inc, o);
-        if (lane >= o) inc += y;
-    }
-    total = __shfl(inc, 63);
-    return inc - x;
+// Exclusive prefix sum over the 64 lanes (and the total in `total`), by row shifts within
+// each 16-lane row, then the broadcasts of a row's last lane into the rows above it.
+__device__ __forceinline__ int wave_excl_scan(int x, int& total) {
+    int v = x;
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);    // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);    // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);    // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);    // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2, 3
+    total = __builtin_amdgcn_readlane(v, 63);
+    return v - x;
 }
 
 __device__ __forceinline__ Cursor cursor_at(const TileEnt* ents, int e, int n) {
@@ -447,11 +449,12 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
     // ---- this workgroup's q-tiles: lane k of wave 0 looks up the k-th ------------------
     // (plan::persist_pos; with per-item lengths for at most kRankedItems items, in the
     // ranked order of plan::ranked_tile)
+    __shared__ __attribute__((aligned(16))) uint32_t s_key[plan::kRankedItems];
     __shared__ int s_order[plan::kRankedItems], s_ne[plan::kRankedItems], s_nrow[plan::kRankedItems];
-    __shared__ int s_i0[plan::kRankedItems], s_i1[plan::kRankedItems];
-    __shared__ long s_start_ne[plan::kRankedItems], s_start_z[plan::kRankedItems];
+    __shared__ int s_tiles[plan::kRankedItems], s_i0[plan::kRankedItems], s_i1[plan::kRankedItems];
+    __shared__ int s_start_ne[plan::kRankedItems], s_start_z[plan::kRankedItems];
     const bool has_len = a.seq_lens != nullptr || a.cu_seqlens != nullptr;
-    const bool ranked = has_len && a.batch <= plan::kRankedItems;
+    const bool ranked = plan::ranked_order(has_len, a.batch, a.n_qtiles, a.q_heads);
     if (wave == 0) {
         const long pk = plan::persist_pos((int)blockIdx.x, lane, (int)gridDim.x, kXcds);
         bool have = false;
@@ -475,39 +478,48 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
             }
             const plan::ItemSched is = lane < B ? plan::item_sched(rows, valid, a.pos_offset, causal, a.window, BM, kBN)
                                                 : plan::ItemSched{0, 0, -1};
+            // rank: the items whose key is above this one's (keys of all 64 lanes, read back
+            // as 16 broadcast reads)
+            typedef __attribute__((address_space(3))) const int lds_int;
+            typedef __attribute__((address_space(3))) const u32x4 lds_key4;
+            const uint32_t key = lane < B ? plan::rank_key(is.cost, lane) : 0u;
+            s_key[lane] = key;
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the writes have landed
+            __builtin_amdgcn_wave_barrier();
             int rank = 0;
-            for (int x = 0; x < B; ++x)
-                rank += plan::ranks_before(__builtin_amdgcn_readlane(is.cost, x), x, is.cost, lane) ? 1 : 0;
+#pragma unroll
+            for (int x4 = 0; x4 < plan::kRankedItems / 4; ++x4) {
+                const u32x4 k4 = ((lds_key4*)(const void*)s_key)[x4];
+                rank += (k4[0] > key ? 1 : 0) + (k4[1] > key ? 1 : 0) + (k4[2] > key ? 1 : 0) + (k4[3] > key ? 1 : 0);
+            }
             if (lane < B) {
                 s_order[rank] = lane;
+                s_tiles[rank] = is.ne * a.q_heads;   // non-empty q-tiles of rank `rank`
                 s_ne[lane] = is.ne;
                 s_nrow[lane] = is.nrow;
                 s_i0[lane] = i0;
                 s_i1[lane] = i1;
             }
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the writes have landed
+            __builtin_amdgcn_s_waitcnt(0xC07F);
             __builtin_amdgcn_wave_barrier();
-            const long tiles_r = lane < B ? (long)s_ne[s_order[lane]] * a.q_heads : 0;   // q-tiles of rank lane
-            const long zeros_b = lane < B ? (long)(is.nrow - is.ne) * a.q_heads : 0;
-            long n_ne = 0, n_z = 0;
-            const long x_ne = wave_excl_scan(tiles_r, lane, n_ne);
-            const long x_z = wave_excl_scan(zeros_b, lane, n_z);
+            int n_ne = 0, n_z = 0;
+            const int x_ne = wave_excl_scan(lane < B ? s_tiles[lane] : 0, n_ne);
+            const int x_z = wave_excl_scan(lane < B ? (is.nrow - is.ne) * a.q_heads : 0, n_z);
             if (lane < B) {
                 s_start_ne[lane] = x_ne;
                 s_start_z[lane] = x_z;
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);
             __builtin_amdgcn_wave_barrier();
-            typedef __attribute__((address_space(3))) const int lds_int;
-            typedef __attribute__((address_space(3))) const long lds_long;
-            const plan::RankedRef rr = plan::ranked_tile(pk, B, a.q_heads, n_ne, n_z, (lds_int*)s_order,
-                                                         (lds_long*)s_start_ne, (lds_long*)s_start_z,
-                                                         (lds_int*)s_ne, (lds_int*)s_nrow);
+            const plan::RankedRef rr =
+                plan::ranked_tile(pk < (long)n_ne + n_z ? (int)pk : -1, B, n_ne, n_z, (lds_int*)s_order,
+                                  (lds_int*)s_start_ne, (lds_int*)s_start_z, (lds_int*)s_ne, (lds_int*)s_nrow);
             if (rr.kind != 2) {
                 have = true;
-                b = rr.b;
-                h = rr.h;
-                qt = rr.qt;
+                // (clamped: an item, head and q-tile of the launch whatever the LDS holds)
+                b = min(max(rr.b, 0), B - 1);
+                h = min(max(rr.h, 0), a.q_heads - 1);
+                qt = min(max(rr.qt, 0), a.n_qtiles - 1);
                 const plan::Layout lay = a.cu_seqlens ? plan::kUnpadded : a.token_major ? plan::kTokenMajor : plan::kHeadMajor;
                 ir = plan::item_rows(lay, b, h, h / (a.q_heads / a.kv_heads), D, a.q_heads, a.kv_heads, a.q_len,
                                      a.kv_len, s_i0[b], s_i1[b], a.seq_lens != nullptr, s_i0[b]);
@@ -545,9 +557,8 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
         const int n0 = __builtin_popcountll(m0);
         if (kind == 0) ents[__builtin_popcountll(m0 & below)] = e;
         if (kind == 1) ents[n0 + __builtin_popcountll(m1 & below)] = e;
-        int steps = kind == 0 ? e.kt_end - e.kt_begin : 0;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) steps += __shfl_xor(steps, o);
+        int steps = 0;   // key tiles of the whole list
+        wave_excl_scan(kind == 0 ? e.kt_end - e.kt_begin : 0, steps);
         if (lane == 0) {
             s_counts[0] = n0;
             s_counts[1] = __builtin_popcountll(m1);
@@ -559,15 +570,22 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
     const int n_zero = uni(s_counts[1]);
     const int n_steps = uni(s_counts[2]);
 
-    // q-tiles whose rows see no key (padded rows, queries past the keys): zeros
-    for (int z = 0; z < n_zero; ++z) {
-        const TileEnt& t = ents[n_ent + z];
-        const int rows = min(BM, uni(t.q_len) - uni(t.q0));
-        uint16_t* o0 = (uint16_t*)a.out + uni64(t.q_base) + (size_t)uni(t.q0) * q_rs;
-        for (int i = tid; i < rows * (D / 8); i += W * 64)
-            *(u32x4*)(o0 + (size_t)(i / (D / 8)) * q_rs + 8 * (i % (D / 8))) = u32x4{0, 0, 0, 0};
+    // q-tiles whose rows see no key (padded rows, queries past the keys): zeros, written
+    // after the workgroup's last key tile (or at once when it has none), so that they do not
+    // delay its first tile copies
+    auto zero_tiles = [&]() {
+        for (int z = 0; z < n_zero; ++z) {
+            const TileEnt& t = ents[n_ent + z];
+            const int rows = min(BM, uni(t.q_len) - uni(t.q0));
+            uint16_t* o0 = (uint16_t*)a.out + uni64(t.q_base) + (size_t)uni(t.q0) * q_rs;
+            for (int i = tid; i < rows * (D / 8); i += W * 64)
+                *(u32x4*)(o0 + (size_t)(i / (D / 8)) * q_rs + 8 * (i % (D / 8))) = u32x4{0, 0, 0, 0};
+        }
+    };
+    if (n_ent == 0) {
+        zero_tiles();
+        return;
     }
-    if (n_ent == 0) return;
 
     // ---- per-lane constants ---------------------------------------------------------------
     st.k_lds0 = lds_addr(k_lds[0]);
@@ -628,7 +646,6 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
         st.hi_r[0] = k.lane.hi;
         st.b_inter_lo[0] = k.inter.lo;
         st.b_inter_hi[0] = k.inter.hi;
-        st.blk_all_rows_valid[0] = k.all_rows_valid;
         return plan::Keys{uni(k.uni.lo), uni(k.uni.hi)};
     };
     // Output of entry e: O / l, zero for rows that see no key, stored with RNE; then the
@@ -640,7 +657,9 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
         const int row = q0 + wave * 32 + (lane & 31);
         const float l_tot = halves_sum(st.l_run[0]);
         const bool sees = plan::row_keys(a.pos_offset + row, kvalid, causal, a.window).hi >= 0;
-        const float inv = (sees && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
+        // a row that sees no key is written as zeros by a select, whatever its (unmasked) sums
+        const bool keep = sees && l_tot > 0.0f;
+        const float inv = keep ? 1.0f / l_tot : 0.0f;
         uint16_t* orow = (uint16_t*)a.out + uni64(ents[e].q_base) + (size_t)min(row, q_len - 1) * q_rs;
         const bool full = q0 + wave * 32 + 32 <= q_len;
         if (full || row < q_len) {
@@ -650,8 +669,8 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
                 for (int e4 = 0; e4 < 4; ++e4) {
                     const int d = 32 * db + 8 * e4 + 4 * g;
                     u32x2 w;
-                    w[0] = H::pack2(st.o[0][db][4 * e4] * inv, st.o[0][db][4 * e4 + 1] * inv);
-                    w[1] = H::pack2(st.o[0][db][4 * e4 + 2] * inv, st.o[0][db][4 * e4 + 3] * inv);
+                    w[0] = H::pack2(keep ? st.o[0][db][4 * e4] * inv : 0.0f, keep ? st.o[0][db][4 * e4 + 1] * inv : 0.0f);
+                    w[1] = H::pack2(keep ? st.o[0][db][4 * e4 + 2] * inv : 0.0f, keep ? st.o[0][db][4 * e4 + 3] * inv : 0.0f);
                     *(u32x2*)(orow + d) = w;
                 }
             }
@@ -769,6 +788,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::MINB) void prefill_bf16_na
     } else {
         step(F_{}, P0{}, sa, sb);
     }
+    zero_tiles();
 }
 
 // Workgroups the device holds at once (Cfg::MINB per CU), per device.

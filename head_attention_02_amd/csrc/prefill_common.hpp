@@ -59,12 +59,14 @@ __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ void keep_branch() { asm volatile("" ::); }
 
 // Per query row block of 32 rows [r0, r0+32) of one (item, head): this lane's key
-// interval, and the keys every / some row of the block sees.
+// interval, and the keys every / some row of the block sees.  Rows that see no key (a
+// position at or past the valid keys, or no query row at all) are written as zeros
+// whatever their scores, so `inter` holds the keys every OTHER row of the block sees: a
+// tile inside it needs no mask for any row whose output is kept.
 struct RowBlockKeys {
     plan::Keys lane;    // this lane's row (empty for a padded row or one past the end)
-    plan::Keys inter;   // keys every row of the block sees (valid when all_rows_valid)
+    plan::Keys inter;   // keys every row of the block that sees a key sees (all keys if none does)
     plan::Keys uni;     // keys some row of the block sees (superset; empty if no row is a query)
-    bool all_rows_valid;
 };
 
 __device__ __forceinline__ RowBlockKeys row_block_keys(const PrefillArgs& a, int r0, int rows, int my_row,
@@ -75,10 +77,11 @@ __device__ __forceinline__ RowBlockKeys row_block_keys(const PrefillArgs& a, int
     if (my_row >= q_len) k.lane.hi = -1;
     const int r1 = min(r0 + rows - 1, q_len - 1);
     const int bp_lo = a.pos_offset + r0, bp_hi = a.pos_offset + r1;
-    k.inter = plan::span_inter(bp_lo, bp_hi, valid, causal, a.window);
+    const int bs_hi = min(bp_hi, valid - 1);   // position of the block's last row that sees a key
+    k.inter = (r0 < q_len && bs_hi >= bp_lo) ? plan::span_inter(bp_lo, bs_hi, valid, causal, a.window)
+                                             : plan::Keys{0, 0x7fffffff};
     k.uni = plan::span_union(bp_lo, bp_hi, valid, causal, a.window);
     if (r0 >= q_len) k.uni.hi = -1;   // no row of the block is a query
-    k.all_rows_valid = r0 < q_len && bp_hi < valid;
     return k;
 }
 

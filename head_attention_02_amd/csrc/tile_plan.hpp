@@ -182,10 +182,21 @@ constexpr ItemSched item_sched(int rows, int valid, int p, bool causal, int wind
 // Whether item a (cost_a) ranks before item b (cost_b).
 constexpr bool ranks_before(int cost_a, int a, int cost_b, int b) { return cost_a > cost_b || (cost_a == cost_b && a < b); }
 
+// The same order as one unsigned key per item (b < kRankedItems, 0 <= cost < 2^25): item a
+// ranks before item b iff rank_key(cost_a, a) > rank_key(cost_b, b); 0 is below every
+// item's key (the kernel gives it to lanes without an item).
+constexpr uint32_t rank_key(int cost, int b) { return ((uint32_t)(cost + 1) << 6) | (uint32_t)(kRankedItems - 1 - b); }
+
+// Whether a launch takes the ranked order: per-item lengths for at most kRankedItems
+// items, and q-tile numbers that fit an int (the kernel numbers them in 32 bits).
+constexpr bool ranked_order(bool has_len, int batch, int n_qtiles, int q_heads) {
+    return has_len && batch <= kRankedItems && (long)batch * n_qtiles * q_heads < (1L << 31);
+}
+
 // The last index i in [0, n) with a[i] <= x (a non-decreasing, a[0] <= x).  P: a pointer
 // or array-like type (the kernel passes LDS pointers).
 template <class P>
-constexpr int last_at_most(P a, int n, long x) {
+constexpr int last_at_most(P a, int n, int x) {
     int lo = 0, hi = n - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) / 2;
@@ -204,21 +215,20 @@ constexpr int last_at_most(P a, int n, long x) {
 struct RankedRef {
     int b, h, qt, kind;
 };
-template <class IP, class LP>
-constexpr RankedRef ranked_tile(long p, int items, int q_heads, long n_ne, long n_z, IP order, LP start_ne,
-                                LP start_z, IP ne, IP nrow) {
+template <class IP>
+constexpr RankedRef ranked_tile(int p, int items, int n_ne, int n_z, IP order, IP start_ne, IP start_z, IP ne,
+                                IP nrow) {
     RankedRef t{0, 0, 0, 2};
-    if (p < n_ne) {
-        const int r = last_at_most(start_ne, items, p);
-        const int b = order[r];
-        const long local = p - start_ne[r];
-        t = {b, (int)(local / ne[b]), ne[b] - 1 - (int)(local % ne[b]), 0};
-    } else if (p < n_ne + n_z) {
-        const long pz = p - n_ne;
-        const int b = last_at_most(start_z, items, pz);
-        const int nz = nrow[b] - ne[b];
-        const long local = pz - start_z[b];
-        t = {b, (int)(local / nz), ne[b] + (int)(local % nz), 1};
+    if (p >= 0 && p - n_ne < n_z) {
+        const bool z = p >= n_ne;   // a zero q-tile
+        const int x = z ? p - n_ne : p;
+        const IP starts = z ? start_z : start_ne;
+        const int r = last_at_most(starts, items, x);
+        const int b = z ? r : order[r];
+        const int n = z ? nrow[b] - ne[b] : ne[b];
+        const int local = x - starts[r];
+        const int h = local / n, i = local - h * n;
+        t = {b, h, z ? ne[b] + i : ne[b] - 1 - i, z ? 1 : 0};
     }
     return t;
 }

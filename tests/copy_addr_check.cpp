@@ -258,10 +258,10 @@ void prefill(const Prefill& p, int slots) {
     } else {
         // the persistent grid: every workgroup's list, at most kMaxList q-tiles long; with
         // per-item lengths for at most kRankedItems items the lists follow the ranked order
-        const bool ranked = !p.lens.empty() && p.B <= kRankedItems;
+        const bool ranked = ranked_order(!p.lens.empty(), p.B, n_qtiles, p.Hq);
         std::vector<int> order(p.B), ne(p.B), nrow(p.B), cost(p.B);
-        std::vector<long> start_ne(p.B), start_z(p.B);
-        long n_ne = 0, n_z = 0;
+        std::vector<int> start_ne(p.B), start_z(p.B);
+        int n_ne = 0, n_z = 0;
         if (ranked) {
             for (int b = 0; b < p.B; ++b) {
                 const int rows = lay == kUnpadded ? imin(imax(p.lens[b], 0), p.Lq) : p.Lq;
@@ -271,18 +271,27 @@ void prefill(const Prefill& p, int slots) {
                 nrow[b] = is.nrow;
                 cost[b] = is.cost;
             }
+            // the kernel ranks by comparing one key per item: the same order as ranks_before
+            std::vector<int> taken(p.B, 0);
             for (int b = 0; b < p.B; ++b) {
                 int rank = 0;
-                for (int x = 0; x < p.B; ++x) rank += ranks_before(cost[x], x, cost[b], b) ? 1 : 0;
+                for (int x = 0; x < p.B; ++x) {
+                    ++g_checks;
+                    const bool before = rank_key(cost[x], x) > rank_key(cost[b], b);
+                    if (before != ranks_before(cost[x], x, cost[b], b)) fail("rank_key disagrees with ranks_before");
+                    rank += before ? 1 : 0;
+                }
+                ++g_checks;
+                if (taken[rank]++) fail("two items of one rank");
                 order[rank] = b;
             }
             for (int r = 0; r < p.B; ++r) {
                 start_ne[r] = n_ne;
-                n_ne += (long)ne[order[r]] * p.Hq;
+                n_ne += ne[order[r]] * p.Hq;
             }
             for (int b = 0; b < p.B; ++b) {
                 start_z[b] = n_z;
-                n_z += (long)(nrow[b] - ne[b]) * p.Hq;
+                n_z += (nrow[b] - ne[b]) * p.Hq;
                 // q-tiles without rows are in no list
                 for (int qt = nrow[b]; qt < n_qtiles; ++qt)
                     for (int h = 0; h < p.Hq; ++h) seen[((size_t)qt * p.B + b) * p.Hq + h] = 1;
@@ -300,8 +309,8 @@ void prefill(const Prefill& p, int slots) {
                 const long pos = persist_pos(wg, k, wgs, 8);
                 TileRef tr{};
                 if (ranked) {
-                    const RankedRef rr = ranked_tile(pos, p.B, p.Hq, n_ne, n_z, order.data(), start_ne.data(),
-                                                     start_z.data(), ne.data(), nrow.data());
+                    const RankedRef rr = ranked_tile(pos < n_ne + n_z ? (int)pos : -1, p.B, n_ne, n_z, order.data(),
+                                                     start_ne.data(), start_z.data(), ne.data(), nrow.data());
                     if (rr.kind == 2) break;
                     tr = {rr.b, rr.h, rr.qt};
                     // the kind the kernel derives from the q-tile's key tiles must agree
