@@ -48,6 +48,9 @@ TM_CASES = [
     (2, 6, 3, 130, 200, 32, True, 70, None, 0, "bf16"),
     (1, 4, 2, 300, 300, 64, True, 0, None, 0, "f16"),
     (2, 2, 1, 70, 90, 128, False, 20, [85, 40], 9, "f32"),
+    # padded items at head dims 128 and 32: whole waves and q-tiles of rows that see no key
+    (2, 8, 2, 300, 300, 128, False, 0, [300, 129], 0, "bf16"),
+    (3, 4, 2, 200, 200, 32, True, 0, [200, 70, 1], 0, "f16"),
 ]
 
 
@@ -61,6 +64,14 @@ def test_token_major_parity(mi, ref, case):
     k = W.draw(rng, (B, Lk, Hkv, D), 1.0, dt)
     v = W.draw(rng, (B, Lk, Hkv, D), 1.0, dt)
     seq = None if sl is None else np.array(sl, np.int32)
+    if seq is not None:
+        # NaN in every query row that sees no key and every key/value row past the valid
+        # ones: such inputs must not reach any output (rows that see no key are written as 0)
+        nan = W.BF16_NAN if dt == "bf16" else np.float32(np.nan)
+        for b in range(B):
+            q[b, max(min(int(seq[b]), Lk) - P, 0):] = nan
+            k[b, max(min(int(seq[b]), Lk), 0):] = nan
+            v[b, max(min(int(seq[b]), Lk), 0):] = nan
     scale = 1.0 / math.sqrt(D)
     kw = dict(pos_offset=P, window=Wn, causal=causal, scale=scale)
     want = ref.prefill_token_major(q, k, v, seq_lens=seq, **kw)
@@ -71,7 +82,11 @@ def test_token_major_parity(mi, ref, case):
                          to_gpu(np.ascontiguousarray(k.transpose(0, 2, 1, 3))),
                          to_gpu(np.ascontiguousarray(v.transpose(0, 2, 1, 3))), seq_lens=sd, **kw)
     torch.cuda.synchronize()
-    check(to_f64(got), want, dt, f"token-major {case}")
+    g = to_f64(got)
+    if seq is not None:
+        for b in range(B):
+            assert np.all(g[b, max(min(int(seq[b]), Lk) - P, 0):] == 0.0), "rows that see no key must be zero"
+    check(g, want, dt, f"token-major {case}")
     assert torch.equal(got, hm.transpose(1, 2).contiguous()), "token-major and head-major launches differ"
 
 
