@@ -4,9 +4,11 @@
 // vector ALUs: each query row is held by eight lanes, each with an eighth of the row's q
 // and output accumulator in registers; a score is the sum of the eight partial dot
 // products (cross-lane adds within the group of eight).  Key/value tiles are staged in
-// LDS and read by the rows' lanes at the same addresses (a broadcast).  Only the keys of
-// the row's key set contribute; tiles outside the union of the rows' key ranges are
-// never loaded.
+// LDS (two buffers; the next tile's loads are in flight while the current one is
+// computed) and read by the rows' lanes at the same addresses (a broadcast).  Only the
+// keys of the row's key set contribute; tiles outside the union of the rows' key ranges
+// are never loaded.  Exponentials are exp2 of scores carried in log2 units (the scale
+// times log2(e) applied to each dot product).
 #include "mi_attn_device.hpp"
 #include "mi_attn_kernels.hpp"
 
@@ -20,8 +22,8 @@ constexpr int kKeys = 32;   // keys per LDS tile
 template <int D>
 __global__ __launch_bounds__(kRows * kLpr) void prefill_f32_kernel(PrefillArgs a) {
     constexpr int DQ = D / kLpr;   // dims per lane
-    __shared__ __attribute__((aligned(16))) float k_lds[kKeys * D];
-    __shared__ __attribute__((aligned(16))) float v_lds[kKeys * D];
+    __shared__ __attribute__((aligned(16))) float k_lds[2][kKeys * D];
+    __shared__ __attribute__((aligned(16))) float v_lds[2][kKeys * D];
 
     const int tid = threadIdx.x;
     const int part = tid % kLpr;
@@ -56,22 +58,42 @@ __global__ __launch_bounds__(kRows * kLpr) void prefill_f32_kernel(PrefillArgs a
     const float* kg = (const float*)a.k + ir.kv_base;
     const float* vg = (const float*)a.v + ir.kv_base;
 
+    // this thread's part of a tile's K and V rows (zero past the valid keys)
+    constexpr int kPer = (kKeys * D / 4 + kRows * kLpr - 1) / (kRows * kLpr);
+    f32x4 kr[kPer], vr[kPer];
+    auto load_tile = [&](int t) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int x = tid + i * kRows * kLpr;
+            const int r = x / (D / 4), c4 = x % (D / 4);
+            const int j = t * kKeys + r;
+            kr[i] = f32x4{0, 0, 0, 0};
+            vr[i] = f32x4{0, 0, 0, 0};
+            if (x < kKeys * D / 4 && j < valid) {
+                kr[i] = *(const f32x4*)(kg + (size_t)j * ir.kv_rs + 4 * c4);
+                vr[i] = *(const f32x4*)(vg + (size_t)j * ir.kv_rs + 4 * c4);
+            }
+        }
+    };
+    const float c2 = a.scale * kLog2e;   // scores in log2 units
     float m_run = kNegInf, l_run = 0.0f;
+    if (tiles.begin < tiles.end) load_tile(tiles.begin);
     for (int t = tiles.begin; t < tiles.end; ++t) {
         const int kbase = t * kKeys;
-        __syncthreads();
-        for (int x = tid; x < kKeys * D / 4; x += kRows * kLpr) {
-            const int r = x / (D / 4), c4 = x % (D / 4);
-            const int j = kbase + r;
-            f32x4 kk = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-            if (j < valid) {
-                kk = *(const f32x4*)(kg + (size_t)j * ir.kv_rs + 4 * c4);
-                vv = *(const f32x4*)(vg + (size_t)j * ir.kv_rs + 4 * c4);
+        float* kb = k_lds[t & 1];
+        float* vb = v_lds[t & 1];
+        __syncthreads();   // nobody still reads this buffer (tile t-2)
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int x = tid + i * kRows * kLpr;
+            if (x < kKeys * D / 4) {
+                const int r = x / (D / 4), c4 = x % (D / 4);
+                *(f32x4*)(kb + r * D + 4 * c4) = kr[i];
+                *(f32x4*)(vb + r * D + 4 * c4) = vr[i];
             }
-            *(f32x4*)(k_lds + r * D + 4 * c4) = kk;
-            *(f32x4*)(v_lds + r * D + 4 * c4) = vv;
         }
         __syncthreads();
+        if (t + 1 < tiles.end) load_tile(t + 1);   // in flight while tile t is computed
 
         float s[kKeys];
         float mx = kNegInf;
@@ -79,25 +101,25 @@ __global__ __launch_bounds__(kRows * kLpr) void prefill_f32_kernel(PrefillArgs a
         for (int jj = 0; jj < kKeys; ++jj) {
             float dot = 0.0f;
 #pragma unroll
-            for (int d = 0; d < DQ; ++d) dot = fmaf(q[d], k_lds[jj * D + part * DQ + d], dot);
+            for (int d = 0; d < DQ; ++d) dot = fmaf(q[d], kb[jj * D + part * DQ + d], dot);
             dot = row_sum<kLpr>(dot);   // the row's eight parts
             const int j = kbase + jj;
-            s[jj] = (j >= lo_r && j <= hi_r) ? dot * a.scale : kNegInf;
+            s[jj] = (j >= lo_r && j <= hi_r) ? dot * c2 : kNegInf;
             mx = fmaxf(mx, s[jj]);
         }
         const float m_new = fmaxf(m_run, mx);
         const float m_use = m_new == kNegInf ? 0.0f : m_new;
-        const float alpha = expf(m_run - m_use);
+        const float alpha = exp2f(m_run - m_use);
         m_run = m_new;
         l_run *= alpha;
 #pragma unroll
         for (int d = 0; d < DQ; ++d) o[d] *= alpha;
 #pragma unroll
         for (int jj = 0; jj < kKeys; ++jj) {
-            const float p = expf(s[jj] - m_use);
+            const float p = exp2f(s[jj] - m_use);
             l_run += p;
 #pragma unroll
-            for (int d = 0; d < DQ; ++d) o[d] = fmaf(p, v_lds[jj * D + part * DQ + d], o[d]);
+            for (int d = 0; d < DQ; ++d) o[d] = fmaf(p, vb[jj * D + part * DQ + d], o[d]);
         }
     }
 
