@@ -3,15 +3,16 @@
 
 One step = one pass over the whole path on resident synthetic inputs: the five named
 configurations, each launched once --
-  C1 tiny_causal_f32     causal MHA, fp32, 2 heads, seq 64, head_dim 32 (latency);
-  C2 bert_base_padded    encoder, bf16, batch 32, 12 heads, head_dim 64, lengths U{16..512};
-  C3 banded_w128_s8192   banded encoder, bf16, batch 8, 12 heads, head_dim 64, |i-j| <= 64;
-  C4 causal_gqa_s4096    causal GQA prefill, bf16, 32 query / 8 KV heads, head_dim 128, 4096;
-  C5 gqa_decode_kv8192   GQA decode, bf16, batch 64, 32/8 heads, head_dim 128, 8192 keys.
+  tiny_causal_f32     causal MHA, fp32, 2 heads, seq 64, head_dim 32 (latency);
+  bert_base_padded    encoder, bf16, batch 32, 12 heads, head_dim 64, lengths U{16..512};
+  banded_w128_s8192   banded encoder, bf16, batch 8, 12 heads, head_dim 64, |i-j| <= 64;
+  causal_gqa_s4096    causal GQA prefill, bf16, 32 query / 8 KV heads, head_dim 128, 4096;
+  gqa_decode_kv8192   GQA decode, bf16, batch 64, 32/8 heads, head_dim 128, 8192 keys.
 Each configuration in turn runs W warm-up launches and then its K timed launches back to
 back, with HIP events recorded on the stream its kernels run on.  Prints one JSON line: `value`
-is C4's throughput in TFLOP/s of algorithmic work (4 * head_dim per unmasked query-key
-pair) with its roofline object, C5's KV-cache bandwidth rides beside it, and `configs`
+is the causal GQA prefill's throughput in TFLOP/s of algorithmic work (4 * head_dim per
+unmasked query-key pair) with its roofline object, the GQA decode's KV-cache bandwidth
+rides beside it, and `configs`
 holds every configuration's time, rate, roofline fraction (against the larger of its MFMA
 and HBM floors) and oracle baseline.  `--workload` benchmarks one named workload alone.
 
@@ -434,8 +435,8 @@ def record_mfma(run_root: Path) -> dict:
 # ---------------------------------------------------------------------------
 
 
-# The five named configurations of one step; `value` is C4's, the decode fields C5's.  The
-# two headline workloads are timed first.
+# The five named configurations of one step; `value` is the causal GQA prefill's, the
+# decode fields the GQA decode's.  The two headline workloads are timed first.
 HEADLINE = ("causal_gqa_s4096", "gqa_decode_kv8192", "tiny_causal_f32", "bert_base_padded", "banded_w128_s8192")
 HEADLINE_VALUE = "causal_gqa_s4096"
 HEADLINE_DECODE = "gqa_decode_kv8192"
@@ -497,11 +498,12 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="headline",
-                    help="headline (the five configurations C1-C5), a name in "
+                    help="headline (the five configurations of one step), a name in "
                          "workloads.WORKLOADS, or copy_calibration (1 GiB device copy for the HBM counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
-                    help="seconds of oracle work for the C4 and C5 baselines (half that for C1-C3)")
+                    help="seconds of oracle work for the causal GQA prefill and GQA decode baselines "
+                         "(half that for the other three)")
     ap.add_argument("--record-traffic", metavar="DIR",
                     help="no GPU run: turn the rocprofv3 FETCH_SIZE / WRITE_SIZE runs under DIR into "
                          "profiles/traffic.json")

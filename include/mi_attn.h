@@ -64,7 +64,7 @@ typedef enum { MI_ATTN_F32 = 0, MI_ATTN_BF16 = 1, MI_ATTN_F16 = 2 } mi_attn_dtyp
 typedef enum {
     MI_ATTN_OK = 0,
     MI_ATTN_ERR_INVALID = 1,     /* bad pointer, size, alignment, or relation between sizes */
-    MI_ATTN_ERR_UNSUPPORTED = 2, /* valid request this build does not implement            */
+    MI_ATTN_ERR_UNSUPPORTED = 2, /* valid request the library does not implement           */
     MI_ATTN_ERR_HIP = 3          /* the HIP runtime refused a launch                       */
 } mi_attn_status;
 

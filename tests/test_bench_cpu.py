@@ -153,26 +153,26 @@ def test_kernel_entry_bounds(monkeypatch):
     # no profiles: the counter fields come back empty
     monkeypatch.setattr(bench, "traffic_from_profiles", lambda *a: None)
     monkeypatch.setattr(bench, "mfma_from_profiles", lambda *a: None)
-    # C4: 137.47 GFLOP over 83.9 MB -> the MFMA floor (55 us) is the larger one
+    # causal GQA prefill: 137.47 GFLOP over 83.9 MB -> the MFMA floor (55 us) is the larger one
     w = W.WORKLOADS["causal_gqa_s4096"]
     fl = 4 * 128 * 32 * 4096 * 4097 / 2
     e = bench.kernel_entry(w, {"seq_lens": None}, 0.110, [0.113, 0.112])
     assert e["bound"] == "mfma" and e["unit"] == "TFLOP/s"
     assert e["achieved"] == pytest.approx(fl / 110e-6 / 1e12)
     assert e["frac"] == pytest.approx(fl / 2.5e15 / 110e-6)
-    # C3: 64 FLOP per byte, below the ridge -> the HBM floor
+    # banded prefill: 64 FLOP per byte, below the ridge -> the HBM floor
     w = W.WORKLOADS["banded_w128_s8192"]
     by = 4 * 8 * 12 * 8192 * 64 * 2
     e = bench.kernel_entry(w, {"seq_lens": None}, 0.1, [0.1])
     assert e["bound"] == "hbm" and e["unit"] == "GB/s"
     assert e["achieved"] == pytest.approx(by / 100e-6 / 1e9)
     assert e["frac"] == pytest.approx(by / 8e12 / 100e-6)
-    # C5: the two caches, 2 GiB, plus Q and O
+    # GQA decode: the two caches, 2 GiB, plus Q and O
     w = W.WORKLOADS["gqa_decode_kv8192"]
     e = bench.kernel_entry(w, {}, 0.3, [0.3])
     assert e["bound"] == "hbm"
     assert e["algorithmic_bytes"] == 2 * 64 * 8 * 8192 * 128 * 2 + 2 * 64 * 32 * 128 * 2
-    # C1: both floors far below a microsecond
+    # tiny fp32 prefill: both floors far below a microsecond
     w = W.WORKLOADS["tiny_causal_f32"]
     e = bench.kernel_entry(w, {"seq_lens": None}, 0.005, [0.008, 0.007])
     assert e["bound"] == "latency" and e["kernel_us"] == pytest.approx(5.0)
