@@ -431,6 +431,28 @@ int main(int argc, char** argv) {
             }
         }
     }
+    // the ranked order's guards and key: q-tile numbers must fit 31 bits, at most
+    // kRankedItems items, lengths given; the key orders as ranks_before up to the largest
+    // cost a 31-bit key count allows
+    {
+        const bool guards[] = {ranked_order(true, 64, 1 << 20, 4096), ranked_order(true, 65, 1, 1),
+                               ranked_order(false, 4, 4, 4), !ranked_order(true, 64, 1 << 12, 8191),
+                               !ranked_order(true, 1, 1, 1)};
+        for (bool bad : guards) {
+            ++g_checks;
+            if (bad) fail("ranked_order guard");
+        }
+        const int costs[] = {0, 1, 2, 63, 64, 65, (1 << 25) - 1, 1 << 25};
+        for (int ca : costs)
+            for (int cb : costs)
+                for (int a = 0; a < kRankedItems; a += 21)
+                    for (int b = 0; b < kRankedItems; b += 13) {
+                        if (a == b) continue;
+                        ++g_checks;
+                        if ((rank_key(ca, a) > rank_key(cb, b)) != ranks_before(ca, a, cb, b)) fail("rank_key order");
+                        if (rank_key(ca, a) == 0u) fail("rank_key zero");
+                    }
+    }
     if (g_fails) {
         std::printf("FAIL total %d violations in %ld checks\n", g_fails, g_checks);
         return 1;
