@@ -87,6 +87,9 @@ PREFILL_CASES = [
     (1, 8, 8, 3000, 3100, 64, False, 100, None, 64, "f16"),
     (2, 4, 4, 777, 777, 64, True, 0, [777, 500], 129, "bf16"),
     (1, 2, 2, 700, 700, 64, False, 0, None, 300, "bf16"),
+    # one KV head for many query heads (32:1 and 16:1)
+    (2, 32, 1, 300, 300, 128, True, 0, None, 0, "bf16"),
+    (3, 16, 1, 200, 200, 64, False, 0, [200, 77, 130], 0, "bf16"),
 ]
 
 
@@ -131,6 +134,9 @@ DECODE_CASES = [
     (128, 8, 4, 64, 64, 128, 40, None, 9, "bf16"),
     (4, 32, 8, 1024, 1000, 128, 999, None, 0, "f16"),
     (3, 12, 4, 512, 512, 32, 0, [512, 100, 3], 64, "f16"),
+    # one KV head for 32 query heads: four groups of 8 heads per key range
+    (2, 32, 1, 600, 600, 128, 0, [600, 301], 0, "bf16"),
+    (3, 32, 1, 400, 400, 64, 399, None, 100, "f16"),
 ]
 
 
